@@ -1,0 +1,145 @@
+/*
+ * nvfp4.h -- C ABI of the NVFP4 W4A4 block-scaled quantization and GEMV/GEMM
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  The page "TensorRT Edge-LLM Completes the MLPerf Edge
+ * Agentic Benchmark 6.4x Faster on Jetson AGX Thor", section "Using NVFP4
+ * quantization to accelerate Qwen3.6-27B inference", runs every linear layer
+ * of the model (language-model head included) with both weights and
+ * activations in NVFP4, the weights quantized once after training, because
+ * low-batch decoding is limited by DRAM bandwidth.  The section "Using
+ * tree-based multi-token prediction to accelerate LLM inference" verifies a
+ * 16-node candidate tree in one forward pass (M = 16 rows), and "Reusing KV
+ * cache across agent turns" prefills only a new suffix (M of a few hundred).
+ * The pages do not spell out NVFP4's bits; this library follows the public
+ * definition:
+ *   - element: E2M1, 4 bits (sign, 2 exponent bits with bias 1, 1 mantissa
+ *     bit); magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6};
+ *   - block scale: one FP8 E4M3FN byte per 16 contiguous K-elements
+ *     (bias 7, subnormals, largest finite 448, 0x7F/0xFF are NaN);
+ *   - tensor scale: one fp32 decode scale g per tensor.
+ *   A quantized value decodes as  x = e2m1(code) * e4m3(scale) * g.
+ *
+ * Quantization of a 16-block x[0..15] (all steps correctly rounded fp32, no
+ * fused multiply-add):
+ *   amax = max|x_i|;   s = (g == 0) ? 0 : (amax / 6) / g
+ *   sb = E4M3(s) rounded to nearest even, saturating at 448;   sv = e4m3(sb)
+ *   d = sv * g;   inv = (d == 0) ? 0 : 1 / d
+ *   code_i = E2M1(x_i * inv) rounded to nearest even, saturating at 6; the
+ *            code's sign bit is the sign bit of x_i * inv (so -0 -> 0x8).
+ * Weights use g_w = amax|W| / 2688 (2688 = 6 * 448), computed on the device.
+ * Activations take a static, calibrated g_a supplied by the caller.
+ *
+ * Layout (row-major, K is the contraction dimension and is contiguous):
+ *   codes  uint8 [rows][K/2]  byte j holds element 2j in its low nibble and
+ *                             element 2j+1 in its high nibble;
+ *   scales uint8 [rows][K/16] one E4M3 byte per block;
+ *   W is [N][K] (one row per output feature), A is [M][K], C is [M][N]:
+ *     C[m][n] = sum_k a_hat[m][k] * w_hat[n][k]
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are device pointers, allocated and owned by the
+ *     caller; the library allocates nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL means
+ *     the default stream) and is stream-ordered; no call synchronizes.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     rejected call enqueues nothing and returns its status; no call aborts.
+ *     A failed kernel launch returns NVFP4_ERR_HIP; faults during execution
+ *     surface at the caller's next synchronization of the stream.
+ *   - Sizes: rows (M, N) >= 0 (0 is a valid empty call); K >= 16 and
+ *     K % 16 == 0; every dimension product must stay below 2^31 elements.
+ *   - Array pointers must be 16-byte aligned; the fp32 tensor-scale pointers
+ *     (a_global, w_global) must be 4-byte aligned.
+ *   - Validation order: dtype/path, shapes, then (for a non-empty call)
+ *     NULL pointers, then alignment.
+ *   - Results are bit-identical from run to run (fixed reduction orders, no
+ *     floating-point atomics on results).
+ *   - Non-finite inputs are outside the contract.
+ *   - Calls are re-entrant; calls on different streams may run concurrently
+ *     as long as they do not write the same buffers.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,   /* a required pointer is NULL                          */
+  NVFP4_ERR_SHAPE = 2,  /* negative size, K < 16, K % 16 != 0, or too large      */
+  NVFP4_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned                      */
+  NVFP4_ERR_DTYPE = 4,  /* unsupported dtype or path selector                    */
+  NVFP4_ERR_HIP = 5     /* the HIP runtime rejected a launch                     */
+} nvfp4_status;
+
+typedef enum {
+  NVFP4_F32 = 0,   /* IEEE binary32                                   */
+  NVFP4_BF16 = 1   /* bfloat16, rounded to nearest even when written  */
+} nvfp4_dtype;
+
+/* Path selector for nvfp4_gemm_ex. */
+typedef enum {
+  NVFP4_PATH_AUTO = 0,    /* M <= 16: skinny path; otherwise the tiled path   */
+  NVFP4_PATH_SKINNY = 1,  /* weight-streaming path, any M (tiles M by 16)     */
+  NVFP4_PATH_TILED = 2    /* LDS-tiled MFMA path, any M                       */
+} nvfp4_path;
+
+/* Offline weight quantization (post-training, done once).
+ *   w         [N][K] in w_dt (NVFP4_F32 or NVFP4_BF16), device.
+ *   w_codes   out: [N][K/2] packed E2M1 codes.
+ *   w_scales  out: [N][K/16] E4M3 block scales.
+ *   w_global  out: one float, g_w = fl32(amax|W| / 2688) (0 for an all-zero W).
+ *             Also used as the accumulator of the amax pass, so it must not
+ *             alias any other argument.
+ * Cites: the page section "Using NVFP4 quantization to accelerate Qwen3.6-27B
+ * inference" (weights quantized once, after training). */
+nvfp4_status nvfp4_quantize_weights(const void* w, nvfp4_dtype w_dt, int64_t N, int64_t K,
+                                    uint8_t* w_codes, uint8_t* w_scales, float* w_global,
+                                    void* stream);
+
+/* On-the-fly activation quantization.
+ *   a         [M][K] in a_dt (NVFP4_F32 or NVFP4_BF16), device.
+ *   a_global  in: one float on the device, the static calibrated decode scale g_a.
+ *   a_codes   out: [M][K/2];  a_scales out: [M][K/16].
+ * Cites: the same section (activations are NVFP4 as well as weights). */
+nvfp4_status nvfp4_quantize_act(const void* a, nvfp4_dtype a_dt, int64_t M, int64_t K,
+                                const float* a_global, uint8_t* a_codes, uint8_t* a_scales,
+                                void* stream);
+
+/* NVFP4 W4A4 GEMM:  out[m][n] = g_a * g_w * sum_k e2m1(qa)*sa * e2m1(qw)*sw.
+ *   a_codes [M][K/2], a_scales [M][K/16], a_global (device float): activations.
+ *   w_codes [N][K/2], w_scales [N][K/16], w_global (device float): weights.
+ *   out     [M][N] in out_dt (NVFP4_F32 or NVFP4_BF16).
+ * Accumulation is in fp32; the result is within 1e-3 * sum_k |a_hat*w_hat| of
+ * the exact product.  M <= 16 (single-stream decode, 16-node tree
+ * verification) runs the weight-streaming skinny path; larger M (suffix
+ * prefill) runs the LDS-tiled MFMA path.
+ * Cites: the sections on NVFP4 quantization, tree-based multi-token
+ * prediction (one pass over 16 candidates) and KV-cache reuse (suffix prefill). */
+nvfp4_status nvfp4_gemm(int64_t M, int64_t K, int64_t N,
+                        const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                        const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                        void* out, nvfp4_dtype out_dt, void* stream);
+
+/* nvfp4_gemm with an explicit path (nvfp4_path); same arguments and result
+ * contract.  Exists so that the two paths can be checked against each other. */
+nvfp4_status nvfp4_gemm_ex(int64_t M, int64_t K, int64_t N,
+                           const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                           void* out, nvfp4_dtype out_dt, int path, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* nvfp4_status_string(nvfp4_status s);
+
+/* ABI version of this header (bumped on any signature change). */
+int nvfp4_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,157 @@
+"""Thin Python binding of the C ABI in include/nvfp4.h (ctypes; marshalling only).
+
+Every function here checks tensor placement, dtype, shape and contiguity,
+allocates outputs with torch (device memory is torch's job), passes raw
+device pointers and the current HIP stream to libnvfp4.so, and raises
+NVFP4Error on a non-zero status.  All arithmetic runs in the library's HIP
+kernels; there is no fallback: without the built library (or without a GPU)
+these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
+
+NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_DTYPE, NVFP4_ERR_HIP = range(6)
+NVFP4_F32, NVFP4_BF16 = 0, 1
+PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
+
+EXPORTS = ("nvfp4_quantize_weights", "nvfp4_quantize_act", "nvfp4_gemm", "nvfp4_gemm_ex",
+           "nvfp4_status_string", "nvfp4_abi_version")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+def load() -> ctypes.CDLL:
+    """Loads libnvfp4.so and declares the signatures (no GPU needed)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with `python -m nvfp4_w4a4_block_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.nvfp4_quantize_weights.argtypes = [p, i32, i64, i64, p, p, p, p]
+    lib.nvfp4_quantize_act.argtypes = [p, i32, i64, i64, p, p, p, p]
+    lib.nvfp4_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, p]
+    lib.nvfp4_gemm_ex.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, i32, p]
+    for f in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "nvfp4_gemm", "nvfp4_gemm_ex"):
+        getattr(lib, f).restype = i32
+    lib.nvfp4_status_string.argtypes = [i32]
+    lib.nvfp4_status_string.restype = ctypes.c_char_p
+    lib.nvfp4_abi_version.argtypes = []
+    lib.nvfp4_abi_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().nvfp4_status_string(status).decode()
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return NVFP4_F32
+    if t == torch.bfloat16:
+        return NVFP4_BF16
+    raise TypeError(f"unsupported dtype {t} (float32 or bfloat16)")
+
+
+def _dev(*ts: torch.Tensor) -> torch.device:
+    dev = ts[0].device
+    for t in ts:
+        if t.device.type != "cuda" or t.device != dev:
+            raise ValueError("all tensors must be on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return dev
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != NVFP4_OK:
+        raise NVFP4Error(status, where)
+
+
+def nvfp4_quantize_weights(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """w [N, K] float32/bfloat16 -> (codes uint8 [N, K/2], scales uint8 [N, K/16], g_w float32 [1])."""
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    dev = _dev(w)
+    N, K = w.shape
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+    g = torch.empty((1,), dtype=torch.float32, device=dev)
+    _check(load().nvfp4_quantize_weights(w.data_ptr(), _dt(w.dtype), N, K, codes.data_ptr(),
+                                         scales.data_ptr(), g.data_ptr(), _stream(dev)),
+           "nvfp4_quantize_weights")
+    return codes, scales, g
+
+
+def nvfp4_quantize_act(a: torch.Tensor, g_a: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                       scales: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """a [M, K] float32/bfloat16 with device decode scale g_a [1] -> (codes [M, K/2], scales [M, K/16])."""
+    if a.dim() != 2:
+        raise ValueError("a must be [M, K]")
+    if g_a.dtype != torch.float32 or g_a.numel() != 1:
+        raise ValueError("g_a must be a float32 tensor of one element")
+    dev = _dev(a, g_a)
+    M, K = a.shape
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    _dev(a, codes, scales)
+    if codes.dtype != torch.uint8 or scales.dtype != torch.uint8 or \
+            codes.numel() != M * (K // 2) or scales.numel() != M * (K // 16):
+        raise ValueError("codes/scales must be uint8 of [M, K/2] / [M, K/16] elements")
+    _check(load().nvfp4_quantize_act(a.data_ptr(), _dt(a.dtype), M, K, g_a.data_ptr(),
+                                     codes.data_ptr(), scales.data_ptr(), _stream(dev)),
+           "nvfp4_quantize_act")
+    return codes, scales
+
+
+def nvfp4_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: torch.Tensor,
+               w_codes: torch.Tensor, w_scales: torch.Tensor, g_w: torch.Tensor,
+               out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+               path: int = PATH_AUTO) -> torch.Tensor:
+    """NVFP4 W4A4 product: out [M, N] = dequant(A) @ dequant(W)^T, fp32 accumulation."""
+    if a_codes.dim() != 2 or w_codes.dim() != 2:
+        raise ValueError("codes must be 2-D")
+    M, K2 = a_codes.shape
+    N = w_codes.shape[0]
+    K = 2 * K2
+    if w_codes.shape[1] != K2 or a_scales.shape != (M, K // 16) or w_scales.shape != (N, K // 16):
+        raise ValueError("inconsistent operand shapes")
+    for t in (a_codes, a_scales, w_codes, w_scales):
+        if t.dtype != torch.uint8:
+            raise ValueError("codes and scales must be uint8")
+    for g in (g_a, g_w):
+        if g.dtype != torch.float32 or g.numel() != 1:
+            raise ValueError("tensor scales must be float32 tensors of one element")
+    dev = _dev(a_codes, a_scales, g_a, w_codes, w_scales, g_w)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    elif out.shape != (M, N) or out.dtype != out_dtype:
+        raise ValueError("out must be [M, N] of out_dtype")
+    _dev(a_codes, out)
+    _check(load().nvfp4_gemm_ex(M, K, N, a_codes.data_ptr(), a_scales.data_ptr(), g_a.data_ptr(),
+                                w_codes.data_ptr(), w_scales.data_ptr(), g_w.data_ptr(),
+                                out.data_ptr(), _dt(out_dtype), path, _stream(dev)),
+           "nvfp4_gemm")
+    return out

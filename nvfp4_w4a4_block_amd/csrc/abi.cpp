@@ -1,0 +1,120 @@
+// C ABI of the NVFP4 library (declared in include/nvfp4.h): argument
+// validation on the host, then dispatch to the HIP kernels.  Validation makes
+// no HIP call, so a rejected call enqueues nothing and is safe without a GPU.
+#include "nvfp4.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;  // exclusive bound on any dimension product
+constexpr int64_t kMaxGridY = 65535;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+bool dtype_ok(int dt) { return dt == NVFP4_F32 || dt == NVFP4_BF16; }
+
+// Checks rows >= 0, K >= 16, K % 16 == 0 and rows * K < 2^31.
+bool shape_ok(int64_t rows, int64_t K) {
+  if (rows < 0 || K < 16 || (K % 16) != 0 || K >= kMaxElems) return false;
+  return rows == 0 || rows < kMaxElems / K;
+}
+
+nvfp4_status from_hip(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(nvfp4_status s) {
+  switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "invalid shape (sizes must be >= 0, K >= 16, K % 16 == 0, products < 2^31)";
+    case NVFP4_ERR_ALIGN: return "pointer not aligned (arrays: 16 bytes, scalars: 4 bytes)";
+    case NVFP4_ERR_DTYPE: return "unsupported dtype or path";
+    case NVFP4_ERR_HIP: return "HIP runtime error while launching";
+  }
+  return "unknown status";
+}
+
+int nvfp4_abi_version(void) { return 1; }
+
+nvfp4_status nvfp4_quantize_weights(const void* w, nvfp4_dtype w_dt, int64_t N, int64_t K,
+                                    uint8_t* w_codes, uint8_t* w_scales, float* w_global,
+                                    void* stream) {
+  if (!dtype_ok(w_dt)) return NVFP4_ERR_DTYPE;
+  if (!shape_ok(N, K)) return NVFP4_ERR_SHAPE;
+  if (!w_global) return NVFP4_ERR_NULL;
+  if (!aligned4(w_global)) return NVFP4_ERR_ALIGN;
+  if (N > 0) {
+    if (!w || !w_codes || !w_scales) return NVFP4_ERR_NULL;
+    if (!aligned16(w) || !aligned16(w_codes) || !aligned16(w_scales)) return NVFP4_ERR_ALIGN;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = w_dt == NVFP4_BF16;
+  hipError_t e = nvfp4::launch_weight_global(w, bf16, N * K, w_global, s);
+  if (e != hipSuccess || N == 0) return from_hip(e);
+  return from_hip(nvfp4::launch_quantize(w, bf16, N, K, w_global, w_codes, w_scales, s));
+}
+
+nvfp4_status nvfp4_quantize_act(const void* a, nvfp4_dtype a_dt, int64_t M, int64_t K,
+                                const float* a_global, uint8_t* a_codes, uint8_t* a_scales,
+                                void* stream) {
+  if (!dtype_ok(a_dt)) return NVFP4_ERR_DTYPE;
+  if (!shape_ok(M, K)) return NVFP4_ERR_SHAPE;
+  if (M == 0) return NVFP4_OK;
+  if (!a || !a_global || !a_codes || !a_scales) return NVFP4_ERR_NULL;
+  if (!aligned16(a) || !aligned4(a_global) || !aligned16(a_codes) || !aligned16(a_scales))
+    return NVFP4_ERR_ALIGN;
+  return from_hip(nvfp4::launch_quantize(a, a_dt == NVFP4_BF16, M, K, a_global, a_codes, a_scales,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_gemm_ex(int64_t M, int64_t K, int64_t N,
+                           const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                           void* out, nvfp4_dtype out_dt, int path, void* stream) {
+  if (!dtype_ok(out_dt)) return NVFP4_ERR_DTYPE;
+  if (path != NVFP4_PATH_AUTO && path != NVFP4_PATH_SKINNY && path != NVFP4_PATH_TILED)
+    return NVFP4_ERR_DTYPE;
+  if (!shape_ok(M, K) || !shape_ok(N, K)) return NVFP4_ERR_SHAPE;
+  if (M > 0 && N >= kMaxElems / M) return NVFP4_ERR_SHAPE;
+  if (path == NVFP4_PATH_AUTO) path = M <= 16 ? NVFP4_PATH_SKINNY : NVFP4_PATH_TILED;
+  if ((path == NVFP4_PATH_SKINNY ? (M + 15) / 16 : (M + 127) / 128) > kMaxGridY)
+    return NVFP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!a_codes || !a_scales || !a_global || !w_codes || !w_scales || !w_global || !out)
+    return NVFP4_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) ||
+      !aligned16(w_scales) || !aligned16(out) || !aligned4(a_global) || !aligned4(w_global))
+    return NVFP4_ERR_ALIGN;
+  nvfp4::GemmArgs g;
+  g.M = (int)M;
+  g.K = (int)K;
+  g.N = (int)N;
+  g.ac = a_codes;
+  g.as = a_scales;
+  g.ga = a_global;
+  g.wc = w_codes;
+  g.ws = w_scales;
+  g.gw = w_global;
+  g.out = out;
+  g.out_bf16 = out_dt == NVFP4_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return from_hip(path == NVFP4_PATH_SKINNY ? nvfp4::launch_gemm_skinny(g, s)
+                                            : nvfp4::launch_gemm_tiled(g, s));
+}
+
+nvfp4_status nvfp4_gemm(int64_t M, int64_t K, int64_t N,
+                        const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                        const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                        void* out, nvfp4_dtype out_dt, void* stream) {
+  return nvfp4_gemm_ex(M, K, N, a_codes, a_scales, a_global, w_codes, w_scales, w_global, out,
+                       out_dt, NVFP4_PATH_AUTO, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Device-side helpers shared by the NVFP4 kernels (gfx950 / CDNA4).
+//
+// NVFP4 as used for weights and activations on the page "TensorRT Edge-LLM
+// Completes the MLPerf Edge Agentic Benchmark 6.4x Faster on Jetson AGX Thor"
+// (section "Using NVFP4 quantization to accelerate Qwen3.6-27B inference"),
+// with the public bit definition: E2M1 elements, one E4M3 scale per 16
+// contiguous K-elements, one fp32 tensor scale.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 16;          // K-elements per E4M3 scale
+constexpr float kE4M3Max = 448.0f;  // largest finite E4M3FN magnitude
+
+// ---------------------------------------------------------------------------
+// Encoders (used by the quantization kernels; every step is exact or
+// correctly rounded fp32, so the bytes are reproducible on any IEEE machine).
+// ---------------------------------------------------------------------------
+
+// Non-negative fp32 -> E4M3FN byte, round to nearest even, saturating at 448.
+// Values below 2^-6 land on the subnormal grid m * 2^-9 (m = 0..8; m = 8 is
+// the smallest normal, whose byte is also 8).  Larger values keep 3 of fp32's
+// 23 mantissa bits with a round-half-even carry into the exponent.
+__device__ __forceinline__ uint32_t e4m3_from_nonneg(float s) {
+  if (!(s < kE4M3Max)) return 0x7Eu;
+  if (s < 0.015625f) return (uint32_t)__builtin_rintf(s * 512.0f);
+  const uint32_t b = __float_as_uint(s);
+  const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+  return ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
+}
+
+// E4M3FN byte (finite) -> fp32, exact (hardware OCP fp8 conversion).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8(byte, 0);
+}
+
+// fp32 -> E2M1 code, round to nearest even, saturating at 6; sign bit taken
+// from the input's sign bit.  Decision points are the midpoints between the
+// magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}; a midpoint goes to the even code
+// (strict '>' where the lower neighbour is even, '>=' where the upper is).
+__device__ __forceinline__ uint32_t e2m1_from_f32(float y) {
+  const float a = __builtin_fabsf(y);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+               (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// ---------------------------------------------------------------------------
+// Dequantization to MFMA operands.
+// ---------------------------------------------------------------------------
+
+// Two E4M3 scale bytes (low two bytes of `w`) -> f16 pair, exact: every E4M3
+// value (2^-9 .. 448) is a normal f16.
+__device__ __forceinline__ h2_t e4m3x2_to_h2(uint32_t w) {
+  const f2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  return h2_t{(_Float16)f.x, (_Float16)f.y};
+}
+
+// Eight packed E2M1 codes (a 32-bit word, element 2j in the low nibble of
+// byte j) times one block scale `s` -> eight f16 values in k order.
+// The gfx950 conversion is exact for a unit scale (it only honours the
+// exponent of its scale operand), so the E4M3 scale is applied with a packed
+// f16 multiply; the product e2m1 * e4m3 has at most 6 significant bits and
+// lies in [2^-10, 2688], so it is exact in f16.
+__device__ __forceinline__ h8_t dequant8(uint32_t w, _Float16 s) {
+  const h2_t s2 = {s, s};
+  const h2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const h2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const h2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const h2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  return h8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ f4_t mfma16x16x32(h8_t a, h8_t b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,37 @@
+// Host-side launchers of the NVFP4 kernels (internal to the library; the
+// public C ABI is include/nvfp4.h).  Arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Per-16-block quantization of a [rows][K] tensor (fp32, or bf16 when `bf16`)
+// with the decode scale read from device memory at `g`.
+hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t K, const float* g,
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+// g = amax|w| / 2688 over `elems` elements, written to the device float `g`.
+hipError_t launch_weight_global(const void* w, bool bf16, int64_t elems, float* g,
+                                hipStream_t stream);
+
+struct GemmArgs {
+  int M, K, N;
+  const uint8_t* ac;  // activation codes [M][K/2]
+  const uint8_t* as;  // activation scales [M][K/16]
+  const float* ga;    // activation decode scale (device)
+  const uint8_t* wc;  // weight codes [N][K/2]
+  const uint8_t* ws;  // weight scales [N][K/16]
+  const float* gw;    // weight decode scale (device)
+  void* out;          // [M][N]
+  bool out_bf16;
+};
+
+// Weight-streaming path (built for M <= 16; tiles larger M by 16 rows).
+hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
+
+// LDS-tiled MFMA path for large M.
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,151 @@
+// NVFP4 quantization kernels for gfx950: weight tensor-scale reduction and
+// the per-16-block quantizer shared by weights and activations.
+//
+// Follows the NVFP4 quantization of weights (once, after training) and of
+// activations on the page "TensorRT Edge-LLM Completes the MLPerf Edge Agentic
+// Benchmark 6.4x Faster on Jetson AGX Thor", section "Using NVFP4 quantization
+// to accelerate Qwen3.6-27B inference".  Every float step is a correctly
+// rounded fp32 operation with no contraction into fused multiply-adds (this
+// file is built with -ffp-contract=off and correctly rounded division), so
+// the codes and scales are reproducible bit for bit.
+#include "device_common.h"
+#include "launch.h"
+
+#pragma clang fp contract(off)
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kQuantThreads = 256;
+
+// Eight consecutive inputs as fp32 (bf16 widens exactly).
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  const f4_t a = *reinterpret_cast<const f4_t*>(p);
+  const f4_t b = *reinterpret_cast<const f4_t*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
+  const u4_t w = *reinterpret_cast<const u4_t*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// One lane quantizes 8 elements; the lane pair (2j, 2j+1) holds 16-block j of
+// the flattened [rows][K] tensor (K % 16 == 0, so blocks never straddle rows).
+// The pair exchanges its partial amax, both lanes derive the same scale, each
+// stores its 4 bytes of packed codes and the even lane stores the scale byte.
+template <typename In>
+__global__ __launch_bounds__(kQuantThreads) void quant_blocks_kernel(
+    const In* __restrict__ x, int64_t n8, const float* __restrict__ g_ptr,
+    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t t = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+  const bool valid = t < n8;
+  float v[8];
+  if (valid) {
+    load8(x + t * 8, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  // n8 is even and waves hold an even number of lanes, so both lanes of a
+  // pair are valid or both are not; every lane takes part in the exchange.
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
+
+  const float g = *g_ptr;
+  const float s = (g == 0.0f) ? 0.0f : (amax / 6.0f) / g;
+  const uint32_t sb = e4m3_from_nonneg(s);
+  const float d = e4m3_to_f32(sb) * g;
+  const float inv = (d == 0.0f) ? 0.0f : 1.0f / d;
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) word |= e2m1_from_f32(v[i] * inv) << (4 * i);
+  if (valid) {
+    codes[t] = word;
+    if ((t & 1) == 0) scales[t >> 1] = (uint8_t)sb;
+  }
+}
+
+__global__ void zero_word_kernel(uint32_t* p) { *p = 0u; }
+
+// Largest |x| over the tensor, accumulated into *acc as fp32 bits with an
+// unsigned atomic max (non-negative floats order like their bit patterns, so
+// the result does not depend on the order of the updates).
+template <typename In>
+__global__ __launch_bounds__(kQuantThreads) void amax_kernel(const In* __restrict__ x, int64_t n8,
+                                                             uint32_t* __restrict__ acc) {
+  float m = 0.0f;
+  for (int64_t t = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; t < n8;
+       t += (int64_t)gridDim.x * kQuantThreads) {
+    float v[8];
+    load8(x + t * 8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+  __shared__ float wave_max[kQuantThreads / 64];
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = wave_max[0];
+#pragma unroll
+    for (int i = 1; i < kQuantThreads / 64; ++i) b = __builtin_fmaxf(b, wave_max[i]);
+    atomicMax(acc, __float_as_uint(b));
+  }
+}
+
+// g_w = fl32(amax / 2688), 2688 = 6 * 448, written over the amax bits.
+__global__ void finalize_global_kernel(uint32_t* p) {
+  const float amax = __uint_as_float(*p);
+  *reinterpret_cast<float*>(p) = amax / 2688.0f;
+}
+
+template <typename In>
+hipError_t launch_quant_blocks(const void* x, int64_t elems, const float* g, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream) {
+  const int64_t n8 = elems / 8;
+  if (n8 == 0) return hipSuccess;
+  const int64_t grid = (n8 + kQuantThreads - 1) / kQuantThreads;
+  quant_blocks_kernel<In><<<dim3((unsigned)grid), dim3(kQuantThreads), 0, stream>>>(
+      static_cast<const In*>(x), n8, g, reinterpret_cast<uint32_t*>(codes), scales);
+  return hipGetLastError();
+}
+
+template <typename In>
+hipError_t launch_amax(const void* x, int64_t elems, uint32_t* acc, hipStream_t stream) {
+  const int64_t n8 = elems / 8;
+  zero_word_kernel<<<1, 1, 0, stream>>>(acc);
+  if (n8 > 0) {
+    int64_t grid = (n8 + kQuantThreads - 1) / kQuantThreads;
+    if (grid > 4096) grid = 4096;  // grid-stride: 16 workgroups per CU is plenty
+    amax_kernel<In><<<dim3((unsigned)grid), dim3(kQuantThreads), 0, stream>>>(
+        static_cast<const In*>(x), n8, acc);
+  }
+  finalize_global_kernel<<<1, 1, 0, stream>>>(acc);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t K, const float* g,
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const int64_t elems = rows * K;
+  return bf16 ? launch_quant_blocks<uint16_t>(x, elems, g, codes, scales, stream)
+              : launch_quant_blocks<float>(x, elems, g, codes, scales, stream);
+}
+
+hipError_t launch_weight_global(const void* w, bool bf16, int64_t elems, float* g,
+                                hipStream_t stream) {
+  uint32_t* acc = reinterpret_cast<uint32_t*>(g);
+  return bf16 ? launch_amax<uint16_t>(w, elems, acc, stream)
+              : launch_amax<float>(w, elems, acc, stream);
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports what include/nvfp4.h declares, and validates arguments
+on the host (CPU only: every call here is rejected, or empty, before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nvfp4_w4a4_block_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "nvfp4.h")
+A16 = 0x10000  # a fake, 16-byte aligned address: never dereferenced by a rejected call
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 6
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in nvfp4.h but not exported"
+    assert sorted(B.EXPORTS) == names
+
+
+def test_exported_symbols_are_c_linkage():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    syms = set(re.findall(r"\b(nvfp4_\w+)\b", out))
+    assert set(declared_functions()) <= syms
+
+
+def test_status_strings_and_version(lib):
+    for s in range(6):
+        assert B.status_string(s)
+    assert B.status_string(99) == "unknown status"
+    assert lib.nvfp4_abi_version() == 1
+
+
+def gemm(lib, M, K, N, ptrs=(A16,) * 7, out_dt=B.NVFP4_BF16, path=B.PATH_AUTO):
+    ac, asc, ga, wc, wsc, gw, out = ptrs
+    return lib.nvfp4_gemm_ex(M, K, N, ac, asc, ga, wc, wsc, gw, out, out_dt, path, None)
+
+
+@pytest.mark.parametrize("K", [0, 8, 15, 17, 24, -16])
+def test_gemm_rejects_bad_k(lib, K):
+    assert gemm(lib, 1, K, 16) == B.NVFP4_ERR_SHAPE
+
+
+def test_gemm_rejects_bad_sizes(lib):
+    assert gemm(lib, -1, 32, 16) == B.NVFP4_ERR_SHAPE
+    assert gemm(lib, 1, 32, -3) == B.NVFP4_ERR_SHAPE
+    assert gemm(lib, 1, 1 << 27, 16) == B.NVFP4_ERR_SHAPE          # N * K = 2^31
+    assert gemm(lib, 1 << 20, 16, 1 << 11) == B.NVFP4_ERR_SHAPE    # M * N = 2^31
+    assert gemm(lib, 1 << 21, 16, 16, path=B.PATH_SKINNY) == B.NVFP4_ERR_SHAPE  # grid rows > 65535
+
+
+def test_gemm_rejects_null_align_dtype_path(lib):
+    assert gemm(lib, 1, 32, 16, ptrs=(A16,) * 6 + (0,)) == B.NVFP4_ERR_NULL
+    assert gemm(lib, 1, 32, 16, ptrs=(0,) + (A16,) * 6) == B.NVFP4_ERR_NULL
+    assert gemm(lib, 1, 32, 16, ptrs=(A16 + 8,) + (A16,) * 6) == B.NVFP4_ERR_ALIGN
+    assert gemm(lib, 1, 32, 16, ptrs=(A16,) * 2 + (A16 + 2,) + (A16,) * 4) == B.NVFP4_ERR_ALIGN
+    # scalar scale pointers only need 4-byte alignment: this one passes validation up to the
+    # dtype check, which fails first here
+    assert gemm(lib, 1, 32, 16, ptrs=(A16,) * 2 + (A16 + 4,) + (A16,) * 4, out_dt=7) == B.NVFP4_ERR_DTYPE
+    assert gemm(lib, 1, 32, 16, path=3) == B.NVFP4_ERR_DTYPE
+    assert lib.nvfp4_gemm(1, 32, 16, A16, A16, A16, A16, A16, A16, A16, 2, None) == B.NVFP4_ERR_DTYPE
+
+
+def test_empty_gemm_is_ok_without_pointers(lib):
+    assert gemm(lib, 0, 32, 16, ptrs=(0,) * 7) == B.NVFP4_OK
+    assert gemm(lib, 4, 32, 0, ptrs=(0,) * 7) == B.NVFP4_OK
+
+
+def test_quantize_validation(lib):
+    q = lib.nvfp4_quantize_act
+    assert q(A16, B.NVFP4_BF16, 1, 20, A16, A16, A16, None) == B.NVFP4_ERR_SHAPE
+    assert q(A16, 5, 1, 32, A16, A16, A16, None) == B.NVFP4_ERR_DTYPE
+    assert q(0, B.NVFP4_F32, 1, 32, A16, A16, A16, None) == B.NVFP4_ERR_NULL
+    assert q(A16, B.NVFP4_F32, 1, 32, 0, A16, A16, None) == B.NVFP4_ERR_NULL
+    assert q(A16 + 4, B.NVFP4_F32, 1, 32, A16, A16, A16, None) == B.NVFP4_ERR_ALIGN
+    assert q(A16, B.NVFP4_F32, 1, 32, A16 + 1, A16, A16, None) == B.NVFP4_ERR_ALIGN
+    assert q(0, B.NVFP4_F32, 0, 32, 0, 0, 0, None) == B.NVFP4_OK           # empty
+    w = lib.nvfp4_quantize_weights
+    assert w(A16, B.NVFP4_F32, 4, 40, A16, A16, A16, None) == B.NVFP4_ERR_SHAPE
+    assert w(A16, 9, 4, 32, A16, A16, A16, None) == B.NVFP4_ERR_DTYPE
+    assert w(A16, B.NVFP4_F32, 4, 32, A16, A16, 0, None) == B.NVFP4_ERR_NULL
+    assert w(0, B.NVFP4_F32, 4, 32, A16, A16, A16, None) == B.NVFP4_ERR_NULL
+    assert w(A16, B.NVFP4_F32, 4, 32, A16 + 8, A16, A16, None) == B.NVFP4_ERR_ALIGN
+    assert w(A16, B.NVFP4_F32, 4, 32, A16, A16, A16 + 2, None) == B.NVFP4_ERR_ALIGN
+    assert w(A16, B.NVFP4_F32, 1 << 16, 1 << 15, A16, A16, A16, None) == B.NVFP4_ERR_SHAPE
+
+
+def test_binding_has_no_cpu_fallback():
+    """The tensor-level functions refuse CPU tensors instead of computing anything."""
+    import torch
+    with pytest.raises(ValueError):
+        B.nvfp4_quantize_weights(torch.zeros(4, 32))
