@@ -42,6 +42,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense f16/bf16 matrix cores
 ROTATE_BYTES = 600 * 2 ** 20   # weight bytes cycled through per pass (> 2x the Infinity Cache)
 DEV = "cuda:0"
+ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
 def log(*a):
@@ -151,6 +152,23 @@ def build_graphs(fn, R: int, total: int):
     return [capture(fn, R), capture(fn, rem) if rem else None]
 
 
+def measured_traffic(wl: WL.Workload):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a copy of known size), or
+    None when there is no summary or the kernel sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as g:
+            h.update(g.read())
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
 def cpu_baseline(wl: WL.Workload, budget_s: float) -> dict:
     """The CPU oracle timed on a bounded sample of the same step: activation quantization plus
     the fp64 product against a sample of pre-quantized weight rows."""
@@ -195,6 +213,9 @@ def main() -> int:
     ap.add_argument("--workload", default="decode_up", choices=sorted(WL.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-reference-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB (a known-size "
+                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -229,7 +250,8 @@ def main() -> int:
                 "unit": "GB/s"}
         metric = "NVFP4 W4A4 GEMV/GEMM HBM GB/s (packed weight codes + block scales per step)"
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(wl)
+    roof["algorithmic_bytes"] = wl.weight_bytes if not wl.chain else None
     line = {
         "metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -239,6 +261,11 @@ def main() -> int:
                    "weight_copies": P.R, "parallelism": "none (1 GPU)"},
         "roofline": roof,
     }
+    if args.copy_reference_mib:
+        x = torch.ones(args.copy_reference_mib * 2 ** 18, dtype=torch.float32, device=DEV)
+        for _ in range(3):
+            x.clone()
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)
