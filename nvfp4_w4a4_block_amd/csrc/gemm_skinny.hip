@@ -41,6 +41,11 @@
 namespace nvfp4 {
 namespace {
 
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  return (s && *s) ? atoi(s) : dflt;
+}
+
 constexpr int kMaxWavesK = 8;
 constexpr uint32_t kOOB = 0x80000000u;  // an offset past every buffer (buffers are < 2^31 bytes)
 
@@ -253,8 +258,39 @@ __device__ __forceinline__ void mma_unit(const USlot<NT>& s, int q, f4_t (&acc)[
   }
 }
 
-template <int NT, int D, bool OUT_BF16>
+// Fragments of the activation operand read from an f16 copy in LDS (see the
+// ALDS mode below): a0 / a1 point at lane (r, q)'s 32 elements of super-step
+// 0 / 1 of the unit (K offsets 32*q and 128 + 32*q), the same slices the
+// weight lanes use; both point at a 64-byte zero run for rows >= M.
+template <int NT>
+__device__ __forceinline__ void mma_unit_lds(const Unit (&w)[NT], const _Float16* a0, const _Float16* a1,
+                                             int q, f4_t (&acc)[NT]) {
+  h2_t sw0[NT], sw1[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) unit_scales(w[t].s, q, sw0[t], sw1[t]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const h8_t af = *reinterpret_cast<const h8_t*>(a0 + 8 * j);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = mfma16x16x32(af, dequant8(w[t].c0[j], sw0[t][j >> 1]), acc[t]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const h8_t af = *reinterpret_cast<const h8_t*>(a1 + 8 * j);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = mfma16x16x32(af, dequant8(w[t].c1[j], sw1[t][j >> 1]), acc[t]);
+  }
+}
+
+// ALDS: the activation rows are few (M * K * 2 bytes fit in LDS), so each wave
+// dequantizes the rows of its own K range once into LDS as f16, and its lanes
+// read ready MFMA fragments (rows >= M read a zero run) instead of converting
+// all 16 rows of the activation operand per weight tile.  Without ALDS the
+// activation runs travel in the ring with the weights and every wave converts
+// them.
+template <int NT, int D, bool ALDS, bool OUT_BF16>
 __global__ __launch_bounds__(64 * kMaxWavesK) void gemm_skinny256_kernel(GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) _Float16 a_lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int KW = blockDim.x >> 6;
@@ -292,11 +328,36 @@ __global__ __launch_bounds__(64 * kMaxWavesK) void gemm_skinny256_kernel(GemmArg
   const int u_begin = (units * wave) / KW, u_end = (units * (wave + 1)) / KW;
   const int my = u_end - u_begin;
 
+  // ALDS fill: rows m_base .. m_base + mrows - 1 of this wave's K range, f16,
+  // row-major with a row stride of (max units per wave) * 256 elements.  A
+  // 64-byte zero run after all waves' rows serves the rows >= M.
+  const int mrows = M - m_base < 16 ? M - m_base : 16;
+  const int u_cap = (units + KW - 1) / KW;
+  const int row_len = u_cap * 256;
+  _Float16* wave_a = a_lds + (size_t)wave * mrows * row_len;
+  const _Float16* zero_run = a_lds + (size_t)KW * mrows * row_len;
+  if constexpr (ALDS) {
+    if (wave == 0 && lane < 16) reinterpret_cast<uint32_t*>(const_cast<_Float16*>(zero_run))[lane] = 0u;
+    const int blocks = mrows * my * 16;  // 16-element blocks to convert
+    for (int b = lane; b < blocks; b += 64) {
+      const int row = b / (my * 16), kb = b - row * (my * 16);
+      const uint32_t g_row = (uint32_t)(m_base + row);
+      const uint32_t k0 = (uint32_t)(u_begin * 256 + kb * 16);
+      const u2_t c = __builtin_amdgcn_raw_buffer_load_b64(ac, g_row * cstride + (k0 >> 1), 0, 0);
+      const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b8(as, g_row * sstride + (k0 >> 4), 0, 0);
+      const _Float16 sc = (_Float16)e4m3_to_f32(sb);
+      h8_t* dst = reinterpret_cast<h8_t*>(wave_a + row * row_len + kb * 16);
+      dst[0] = dequant8(c.x, sc);
+      dst[1] = dequant8(c.y, sc);
+    }
+    __syncthreads();  // the zero run is written by wave 0
+  }
+
   auto load_slot = [&](int i) {
     USlot<NT> s;
     const bool ok = i < my;
     const uint32_t u = (uint32_t)(u_begin + i);
-    s.a = load_unit(ac, as, a_c + u * 128, a_s + u * 16, ok && a_ok);
+    if constexpr (!ALDS) s.a = load_unit(ac, as, a_c + u * 128, a_s + u * 16, ok && a_ok);
 #pragma unroll
     for (int t = 0; t < NT; ++t) s.w[t] = load_unit(wc, ws, w_c[t] + u * 128, w_s[t] + u * 16, ok && w_ok[t]);
     return s;
@@ -315,7 +376,16 @@ __global__ __launch_bounds__(64 * kMaxWavesK) void gemm_skinny256_kernel(GemmArg
   for (int i0 = 0; i0 < my; i0 += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
-      if (i0 + j < my) mma_unit<NT>(ring[j], q, acc);
+      if (i0 + j < my) {
+        if constexpr (ALDS) {
+          const bool live = r < mrows;
+          const _Float16* a0 = live ? wave_a + r * row_len + (i0 + j) * 256 + 32 * q : zero_run;
+          const _Float16* a1 = live ? a0 + 128 : zero_run;
+          mma_unit_lds<NT>(ring[j].w, a0, a1, q, acc);
+        } else {
+          mma_unit<NT>(ring[j], q, acc);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
       ring[j] = load_slot(i0 + j + D);
       __builtin_amdgcn_sched_barrier(0);
@@ -356,10 +426,429 @@ __global__ __launch_bounds__(64 * kMaxWavesK) void gemm_skinny256_kernel(GemmArg
   }
 }
 
-int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  return (s && *s) ? atoi(s) : dflt;
+// ---------------------------------------------------------------------------
+// VALU GEMV for M <= 2 and K % 512 == 0 (single-stream decode).  With one or
+// two activation rows the MFMA's 16-row operand would be mostly padding and,
+// worse, its lane layout limits a load instruction to 64 bytes per weight row.
+// Here the lane layout is free: 16 lanes share a weight row and read 256
+// contiguous bytes (512 codes) of it per instruction, 4 rows per instruction,
+// and each lane reads the 2 scale bytes of its 32 codes (32 contiguous bytes
+// per row).
+//
+// The workgroup first dequantizes the activation rows once into LDS as f16
+// (a = e2m1 * s_a, exact) and every wave reads its 32 values per segment from
+// there.  A wave owns 4*G weight rows over the whole of K and streams its
+// (segment) units through a ring of D units of loads, so memory and
+// arithmetic overlap for the wave's whole life and no partial sums cross
+// waves.  Arithmetic: each weight byte becomes an f16 pair (exact), v_dot2
+// f16 -> fp32 accumulates 8 pairs per 16-block, the block's weight scale is
+// applied with one fp32 FMA, and the 16 lanes of a row are summed at the end
+// in a fixed order; g_a * g_w in the epilogue.
+// ---------------------------------------------------------------------------
+template <int G>
+struct GUnit {
+  u4_t c[G];
+};
+
+template <int MR, int G, int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void gemv_valu_kernel(GemmArgs p) {
+  extern __shared__ __attribute__((aligned(16))) h2_t a_pairs[];  // [MR][K/2]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, rr = lane >> 4;
+  const int M = p.M, K = p.K, N = p.N;
+  const uint32_t cstride = (uint32_t)K >> 1, sstride = (uint32_t)K >> 4;
+  const int segs = K >> 9;
+  const int n0 = (blockIdx.x * (blockDim.x >> 6) + wave) * (4 * G);
+
+  const __amdgpu_buffer_rsrc_t ac = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.ac), (short)0, (int)((uint32_t)M * cstride), 0x00020000);
+  const __amdgpu_buffer_rsrc_t as = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.as), (short)0, (int)((uint32_t)M * sstride), 0x00020000);
+  const __amdgpu_buffer_rsrc_t wc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.wc), (short)0, (int)((uint32_t)N * cstride), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.ws), (short)0, (int)((uint32_t)N * sstride), 0x00020000);
+
+  // Rows past N lie past the end of the weight buffers and read as zeros.
+  auto load_unit = [&](int seg) {
+    GUnit<G> u;
+    const bool ok = seg < segs;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint32_t row = (uint32_t)(n0 + 4 * g + rr);
+      u.c[g] = __builtin_amdgcn_raw_buffer_load_b128(wc, ok ? row * cstride + (uint32_t)seg * 256 + 16 * c : kOOB, 0, 0);
+    }
+    return u;
+  };
+
+  // Weight loads first (the long latency), then the activation fill.
+  GUnit<G> ring[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    ring[j] = load_unit(j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // The wave's rows are consecutive, so their scale bytes are one contiguous
+  // run of 4*G*K/16 bytes: a few full 16-byte-per-lane loads stage it in the
+  // wave's LDS region (instead of a 2-byte load per lane, row and segment).
+  uint8_t* wave_sc = reinterpret_cast<uint8_t*>(a_pairs + M * cstride) + wave * (4 * G) * sstride;
+  {
+    const uint32_t run = (uint32_t)(4 * G) * sstride, base = (uint32_t)n0 * sstride;
+    for (uint32_t off = 16 * lane; off < run; off += 1024) {
+      const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(ws, base + off, 0, 0);
+      *reinterpret_cast<u4_t*>(wave_sc + off) = v;
+    }
+  }
+  const int a_blocks = M * (K >> 4);
+  for (int blk = threadIdx.x; blk < a_blocks; blk += blockDim.x) {
+    const uint32_t m = (uint32_t)blk / sstride, kb = (uint32_t)blk - m * sstride;
+    const u2_t cc = __builtin_amdgcn_raw_buffer_load_b64(ac, m * cstride + kb * 8, 0, 0);
+    const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b8(as, m * sstride + kb, 0, 0);
+    const _Float16 sc = (_Float16)e4m3_to_f32(sb);
+    h8_t* dst = reinterpret_cast<h8_t*>(a_pairs + m * cstride + kb * 8);
+    dst[0] = dequant8(cc.x, sc);
+    dst[1] = dequant8(cc.y, sc);
+  }
+  __syncthreads();
+
+  float acc[G][MR];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[g][m] = 0.f;
+
+  auto compute_unit = [&](const GUnit<G>& u, int seg) {
+    h2_t av[MR][16];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const h8_t* src = reinterpret_cast<const h8_t*>(a_pairs + (m < M ? m : 0) * cstride + seg * 256 + 16 * c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const h8_t v = src[i];
+        av[m][4 * i + 0] = h2_t{v[0], v[1]};
+        av[m][4 * i + 1] = h2_t{v[2], v[3]};
+        av[m][4 * i + 2] = h2_t{v[4], v[5]};
+        av[m][4 * i + 3] = h2_t{v[6], v[7]};
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint32_t sb = *reinterpret_cast<const uint16_t*>(wave_sc + (4 * g + rr) * sstride + seg * 32 + 2 * c);
+      const f2_t sw = __builtin_amdgcn_cvt_pk_f32_fp8(sb, false);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        float part[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) part[m] = 0.f;
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const uint32_t word = u.c[g][2 * b + d];
+          const h2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0);
+          const h2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1);
+          const h2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2);
+          const h2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3);
+#pragma unroll
+          for (int m = 0; m < MR; ++m) {
+            const int e = 8 * b + 4 * d;
+            part[m] = __builtin_amdgcn_fdot2(av[m][e + 0], w0, part[m], false);
+            part[m] = __builtin_amdgcn_fdot2(av[m][e + 1], w1, part[m], false);
+            part[m] = __builtin_amdgcn_fdot2(av[m][e + 2], w2, part[m], false);
+            part[m] = __builtin_amdgcn_fdot2(av[m][e + 3], w3, part[m], false);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[g][m] = __builtin_fmaf(part[m], b ? sw.y : sw.x, acc[g][m]);
+      }
+    }
+  };
+
+  for (int i0 = 0; i0 < segs; i0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      if (i0 + j < segs) compute_unit(ring[j], i0 + j);
+      __builtin_amdgcn_sched_barrier(0);
+      ring[j] = load_unit(i0 + j + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Sum the 16 lanes of each row in a fixed order; lane c == 0 stores.
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) acc[g][m] += __shfl_xor(acc[g][m], off, 16);
+  if (c != 0) return;
+  const float gg = (*p.ga) * (*p.gw);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int n = n0 + 4 * g + rr;
+    if (n >= N) continue;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      if (m >= M) continue;
+      const float v = acc[g][m] * gg;
+      const int64_t o = (int64_t)m * N + n;
+      if constexpr (OUT_BF16) {
+        reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(v);
+      } else {
+        reinterpret_cast<float*>(p.out)[o] = v;
+      }
+    }
+  }
 }
+
+template <int MR, int G, int D>
+hipError_t launch_gemv(const GemmArgs& a, int waves_per_wg, hipStream_t stream) {
+  const int64_t groups = (a.N + 4 * G - 1) / (4 * G);
+  const dim3 grid((unsigned)((groups + waves_per_wg - 1) / waves_per_wg));
+  const size_t lds = (size_t)MR * a.K * 2 + (size_t)waves_per_wg * 4 * G * (a.K / 16);  // f16 activation rows + scale runs
+  if (a.out_bf16) gemv_valu_kernel<MR, G, D, true><<<grid, 64 * waves_per_wg, lds, stream>>>(a);
+  else gemv_valu_kernel<MR, G, D, false><<<grid, 64 * waves_per_wg, lds, stream>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Memory-order GEMV for M <= 2 (single-stream decode), K >= 2048, K % 256 == 0.
+// Measured on MI355X: reading the weight matrix as many rows at once in
+// 256-byte pieces leaves DRAM pages mostly unused (request latency ~3x that
+// of a sequential read), so here every wave streams a contiguous run of R
+// whole rows in memory order, 1 KB per instruction (lane l takes 16 bytes =
+// 32 codes).  Chunk q of the run belongs to row
+// q / (K/32) at K offset 32 * (q % (K/32)); its activation values come from
+// an f16 copy in LDS.  Its two scale bytes sit at byte 2q of the scale array,
+// so the scales of 8 instructions form one contiguous kilobyte, fetched with
+// a single 16-byte-per-lane load and staged in LDS (per-lane 2-byte loads
+// of the scales cost as much time as the codes themselves).  Each lane accumulates the chunks of its current row
+// and, when its row changes, parks the partial sum in a per-row LDS slot;
+// the R row sums are then added over the 64 slots in a fixed order, so the
+// result does not depend on timing.  Arithmetic as in the other GEMVs: exact
+// f16 pairs, v_dot2 into fp32 per 16-block, one FMA with the block scale.
+// ---------------------------------------------------------------------------
+constexpr int kFlatAB = 8;  // activation blocks per thread in the fill
+
+template <int MR, int CPOL, bool OUT_BF16>
+__global__ __launch_bounds__(512) void gemv_flat_kernel(GemmArgs p, int R) {
+  // LDS: f16 activations as 4 planes per row, [m][t][chunk][8 values] with
+  // plane t holding elements 8t..8t+7 of every 32-element chunk, so that a
+  // lane reading its chunk's plane t reads the 16 bytes next to its
+  // neighbours' (conflict-free); then the per-wave row slots.
+  extern __shared__ __attribute__((aligned(16))) h8_t fa_planes[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int M = p.M, K = p.K, N = p.N;
+  const uint32_t cstride = (uint32_t)K >> 1, sstride = (uint32_t)K >> 4;
+  const int cpr = K >> 5;                        // 16-byte chunks per row
+  const int row0 = (blockIdx.x * (blockDim.x >> 6) + wave) * R;
+  const int n_chunks = R * cpr;                  // chunks of this wave's run
+  const int n_instr = (n_chunks + 63) >> 6;
+  const uint32_t qbase = (uint32_t)row0 * (uint32_t)cpr;
+
+  const __amdgpu_buffer_rsrc_t ac = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.ac), (short)0, (int)((uint32_t)M * cstride), 0x00020000);
+  const __amdgpu_buffer_rsrc_t as = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.as), (short)0, (int)((uint32_t)M * sstride), 0x00020000);
+  const __amdgpu_buffer_rsrc_t wc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.wc), (short)0, (int)((uint32_t)N * cstride), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.ws), (short)0, (int)((uint32_t)N * sstride), 0x00020000);
+
+  // Chunks past the run (or rows past N, which lie past the buffers) read zeros.
+  auto load = [&](int i) {
+    const int qi = 64 * i + lane;
+    const bool ok = i < n_instr && qi < n_chunks;
+    const uint32_t q = qbase + (uint32_t)qi;
+    return __builtin_amdgcn_raw_buffer_load_b128(wc, ok ? q * 16 : kOOB, 0, CPOL);
+  };
+  // The two scale bytes of chunk q sit at byte 2q of the scale array, so the
+  // scales of 8 consecutive instructions (512 chunks) are one contiguous
+  // kilobyte: one 16-byte load per lane fetches them, and the wave parks them
+  // in its own LDS kilobyte.  With K % 256 == 0 every window starts on a
+  // 16-byte boundary and the array length is a multiple of 16, so a lane's
+  // load lies wholly inside or wholly past the array (the buffer range check
+  // zeroes a load that crosses the end, in-range bytes included).
+  const uint32_t s_total = (uint32_t)N * sstride;
+  auto load_scales = [&](int g) {
+    const uint32_t off = 2 * (qbase + 512 * (uint32_t)g) + 16 * lane;
+    const bool ok = 512 * g + 8 * lane < n_chunks && off < s_total;
+    return __builtin_amdgcn_raw_buffer_load_b128(ws, ok ? off : kOOB, 0, CPOL);
+  };
+
+  // Activation blocks of this thread first (straight-line: a fixed number of
+  // loads, blocks past the end read zeros), then the weight ring, so that
+  // the fill below waits for the activation loads only.
+  const int a_blocks = M * (K >> 4);
+  u2_t a_code[kFlatAB];
+  uint32_t a_sb[kFlatAB];
+#pragma unroll
+  for (int t = 0; t < kFlatAB; ++t) {
+    const uint32_t blk = threadIdx.x + t * blockDim.x;
+    const bool ok = (int)blk < a_blocks;
+    const uint32_t m = blk / sstride, kb = blk - m * sstride;
+    a_code[t] = __builtin_amdgcn_raw_buffer_load_b64(ac, ok ? m * cstride + kb * 8 : kOOB, 0, 0);
+    a_sb[t] = __builtin_amdgcn_raw_buffer_load_b8(as, ok ? m * sstride + kb : kOOB, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  u4_t sreg = load_scales(0);
+  __builtin_amdgcn_sched_barrier(0);
+  u4_t ring[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ring[j] = load(j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // f16 activation planes (once per workgroup).
+#pragma unroll
+  for (int t = 0; t < kFlatAB; ++t) {
+    const uint32_t blk = threadIdx.x + t * blockDim.x;
+    if ((int)blk < a_blocks) {
+      const uint32_t m = blk / sstride, kb = blk - m * sstride;
+      const _Float16 sc = (_Float16)e4m3_to_f32(a_sb[t]);
+      const uint32_t chunk = kb >> 1, t0 = 2 * (kb & 1);
+      fa_planes[(m * 4 + t0) * cpr + chunk] = dequant8(a_code[t].x, sc);
+      fa_planes[(m * 4 + t0 + 1) * cpr + chunk] = dequant8(a_code[t].y, sc);
+    }
+  }
+  float* slots = reinterpret_cast<float*>(fa_planes + M * 4 * cpr) + wave * (R * MR * 64);
+  u4_t* s_stage = reinterpret_cast<u4_t*>(reinterpret_cast<float*>(fa_planes + M * 4 * cpr) + (blockDim.x >> 6) * (R * MR * 64)) + wave * 64;
+  const uint16_t* s_bytes = reinterpret_cast<const uint16_t*>(s_stage);
+  for (int j = 0; j < R * MR; ++j) slots[j * 64 + lane] = 0.f;
+  __syncthreads();
+
+  // Lane state: its current row (local) and K-chunk within that row.
+  int row_l = lane / cpr;
+  int kc = lane - row_l * cpr;
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+
+  auto consume = [&](const u4_t& c, int j) {
+    h8_t av[MR][4];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) av[m][t] = fa_planes[((m < M ? m : 0) * 4 + t) * cpr + kc];
+    const f2_t sw = __builtin_amdgcn_cvt_pk_f32_fp8(s_bytes[64 * j + lane], false);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float p0[MR], p1[MR];
+#pragma unroll
+      for (int m = 0; m < MR; ++m) { p0[m] = 0.f; p1[m] = 0.f; }
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const uint32_t word = c[2 * b + d];
+        const h2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0);
+        const h2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1);
+        const h2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2);
+        const h2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          const h8_t& v = av[m][2 * b + d];   // plane 2b+d: elements 16b + 8d .. +7
+          p0[m] = __builtin_amdgcn_fdot2(h2_t{v[0], v[1]}, w0, p0[m], false);
+          p1[m] = __builtin_amdgcn_fdot2(h2_t{v[2], v[3]}, w1, p1[m], false);
+          p0[m] = __builtin_amdgcn_fdot2(h2_t{v[4], v[5]}, w2, p0[m], false);
+          p1[m] = __builtin_amdgcn_fdot2(h2_t{v[6], v[7]}, w3, p1[m], false);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < MR; ++m) acc[m] = __builtin_fmaf(p0[m] + p1[m], b ? sw.y : sw.x, acc[m]);
+    }
+    // advance to the next instruction's chunk (64 chunks later; cpr >= 64)
+    kc += 64;
+    if (kc >= cpr) {
+      if (row_l < R) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) slots[(row_l * MR + m) * 64 + lane] = acc[m];
+      }
+#pragma unroll
+      for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+      kc -= cpr;
+      ++row_l;
+    }
+  };
+
+  for (int i0 = 0; i0 < n_instr; i0 += 8) {
+    s_stage[lane] = sreg;              // scales of instructions i0 .. i0+7
+    sreg = load_scales((i0 >> 3) + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (i0 + j < n_instr) consume(ring[j], j);
+      __builtin_amdgcn_sched_barrier(0);
+      ring[j] = load(i0 + j + 8);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (row_l < R) {  // the last row of this lane, if it did not wrap at the end
+#pragma unroll
+    for (int m = 0; m < MR; ++m) slots[(row_l * MR + m) * 64 + lane] = acc[m];
+  }
+  // Same-wave LDS ops are ordered; row (lane / MR, m = lane % MR) sums its 64 slots in order.
+  if (lane >= R * MR) return;
+  const int row = lane / MR, m = lane % MR;
+  const f4_t* sl = reinterpret_cast<const f4_t*>(slots + (row * MR + m) * 64);
+  float sum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const f4_t v = sl[t];
+    sum += v.x; sum += v.y; sum += v.z; sum += v.w;
+  }
+  const int n = row0 + row;
+  if (n < N && m < M) {
+    const float v = sum * ((*p.ga) * (*p.gw));
+    const int64_t o = (int64_t)m * N + n;
+    if constexpr (OUT_BF16) {
+      reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(v);
+    } else {
+      reinterpret_cast<float*>(p.out)[o] = v;
+    }
+  }
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+// Rows per wave for the memory-order GEMV: the grid is a whole multiple
+// (`per_cu`) of the compute-unit count, so that every CU streams the same
+// number of rows (a grid of, say, 1.5 workgroups per CU leaves half the CUs
+// idle for the last third of the kernel).
+int flat_rows_per_wave(const GemmArgs& a, int waves_per_wg, int per_cu) {
+  const int64_t waves = (int64_t)device_cus() * per_cu * waves_per_wg;
+  return (int)((a.N + waves - 1) / waves);
+}
+
+size_t flat_lds_bytes(const GemmArgs& a, int waves_per_wg, int R, int MR) {
+  return (size_t)MR * a.K * 2 + (size_t)waves_per_wg * (R * MR * 64 * 4 + 1024);
+}
+
+template <int MR>
+hipError_t launch_gemv_flat(const GemmArgs& a, int waves_per_wg, int R, hipStream_t stream) {
+  const int64_t waves = (a.N + R - 1) / R;
+  const dim3 grid((unsigned)((waves + waves_per_wg - 1) / waves_per_wg));
+  const size_t lds = flat_lds_bytes(a, waves_per_wg, R, MR);
+  const bool nt = env_int("NVFP4_FLAT_NT", 1) != 0;  // non-temporal weight stream
+  if (a.out_bf16) {
+    if (nt) gemv_flat_kernel<MR, 2, true><<<grid, 64 * waves_per_wg, lds, stream>>>(a, R);
+    else gemv_flat_kernel<MR, 0, true><<<grid, 64 * waves_per_wg, lds, stream>>>(a, R);
+  } else {
+    if (nt) gemv_flat_kernel<MR, 2, false><<<grid, 64 * waves_per_wg, lds, stream>>>(a, R);
+    else gemv_flat_kernel<MR, 0, false><<<grid, 64 * waves_per_wg, lds, stream>>>(a, R);
+  }
+  return hipGetLastError();
+}
+
 
 template <int NT, int VB, int D>
 hipError_t launch_cfg(const GemmArgs& a, int kw, hipStream_t stream) {
@@ -384,16 +873,30 @@ hipError_t launch_vb(const GemmArgs& a, int nt, int kw, hipStream_t stream) {
 
 }  // namespace
 
-template <int NT, int D>
+// Dynamic LDS of the ALDS mode: every wave's f16 activation rows plus the
+// 64-byte zero run (must match the layout in the kernel).
+size_t alds_bytes(const GemmArgs& a, int kw) {
+  const int units = a.K / 256;
+  const int mrows = a.M < 16 ? a.M : 16;
+  return (size_t)kw * mrows * ((units + kw - 1) / kw) * 256 * 2 + 64;
+}
+
+template <int NT, int D, bool ALDS>
 hipError_t launch256(const GemmArgs& a, int kw, hipStream_t stream) {
   const dim3 grid((unsigned)((a.N + 16 * NT - 1) / (16 * NT)), (unsigned)((a.M + 15) / 16));
   const dim3 block(64 * kw);
+  const size_t lds = ALDS ? alds_bytes(a, kw) : 0;
   if (a.out_bf16) {
-    gemm_skinny256_kernel<NT, D, true><<<grid, block, 0, stream>>>(a);
+    gemm_skinny256_kernel<NT, D, ALDS, true><<<grid, block, lds, stream>>>(a);
   } else {
-    gemm_skinny256_kernel<NT, D, false><<<grid, block, 0, stream>>>(a);
+    gemm_skinny256_kernel<NT, D, ALDS, false><<<grid, block, lds, stream>>>(a);
   }
   return hipGetLastError();
+}
+
+template <int NT, int D>
+hipError_t launch256(const GemmArgs& a, int kw, bool alds, hipStream_t stream) {
+  return alds ? launch256<NT, D, true>(a, kw, stream) : launch256<NT, D, false>(a, kw, stream);
 }
 
 // Launch choice.  K % 256 == 0 takes the fast path.  Measured on MI355X
@@ -411,27 +914,59 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   const int e_kw = env_int("NVFP4_SKINNY_KW", 0);
   const int e_d = env_int("NVFP4_SKINNY_D", 0);
   const bool kw_ok = e_kw == 1 || e_kw == 2 || e_kw == 4 || e_kw == 8;
+  // VALU GEMV for one or two activation rows (K a multiple of 512 and the
+  // f16 activation rows within 64 KiB of LDS).  NVFP4_GEMV=0 disables it;
+  // NVFP4_GEMV_G (rows per wave / 4) and NVFP4_GEMV_W (waves per workgroup)
+  // are tuning knobs.
+  const int e_gemv = env_int("NVFP4_GEMV", 2);
+  if (e_gemv == 2 && a.M <= 2 && a.K >= 2048 && a.K % 256 == 0) {
+    int e_w = env_int("NVFP4_GEMV_W", 4);
+    if (e_w != 4 && e_w != 8) e_w = 4;
+    int R = flat_rows_per_wave(a, e_w, env_int("NVFP4_FLAT_C", 1));
+    if (R < 1) R = 1;
+    if (R * a.M <= 64 && flat_lds_bytes(a, e_w, R, a.M) <= 64 * 1024 &&
+        (int64_t)a.M * (a.K / 16) <= (int64_t)64 * e_w * kFlatAB) {
+      return a.M == 1 ? launch_gemv_flat<1>(a, e_w, R, stream) : launch_gemv_flat<2>(a, e_w, R, stream);
+    }
+  }
+  if (e_gemv != 0 && a.M <= 2 && a.K % 512 == 0 && (int64_t)a.M * a.K * 2 + 4 * 16 * (a.K / 16) <= 64 * 1024) {
+    const int e_g = env_int("NVFP4_GEMV_G", 2);
+    int e_w = env_int("NVFP4_GEMV_W", 4);
+    if (e_w != 1 && e_w != 2 && e_w != 4) e_w = 4;
+    if (a.M == 1) {
+      if (e_g == 1) return launch_gemv<1, 1, 4>(a, e_w, stream);
+      if (e_g == 4) return launch_gemv<1, 4, 3>(a, e_w, stream);
+      return launch_gemv<1, 2, 4>(a, e_w, stream);
+    }
+    return launch_gemv<2, 2, 4>(a, e_w, stream);
+  }
   if (a.K % 256 == 0) {
     int nt = a.M > 1 ? 2 : 1;
     if (e_nt == 1 || e_nt == 2) nt = e_nt;
     const int64_t wgs = ((tiles16 + nt - 1) / nt) * mtiles;
     const int64_t units = a.K / 256;
+    // activations in LDS when they are few: a handful of rows whose f16 copy
+    // stays small (measured faster for M = 1; M = 16 streams them instead)
+    const bool small_m = a.M <= 4;
     int kw = 1;
-    while (kw < kMaxWavesK && wgs * kw < 600 && units / (2 * kw) >= 4) kw *= 2;
+    while (kw < kMaxWavesK && (small_m ? wgs * kw < 4096 : wgs * kw < 600) && units / (2 * kw) >= 4) kw *= 2;
     if (kw_ok) kw = e_kw;
+    const int e_alds = env_int("NVFP4_SKINNY_ALDS", -1);
+    bool alds = small_m && alds_bytes(a, kw) <= 48 * 1024;
+    if (e_alds == 0 || e_alds == 1) alds = e_alds == 1 && alds_bytes(a, kw) <= 48 * 1024;
     const int d = (e_d == 2 || e_d == 3 || e_d == 4 || e_d == 6) ? e_d : (nt == 1 ? 3 : 2);
     if (nt == 2) {
       switch (d) {
-        case 3: return launch256<2, 3>(a, kw, stream);
-        case 4: case 6: return launch256<2, 4>(a, kw, stream);
-        default: return launch256<2, 2>(a, kw, stream);
+        case 3: return launch256<2, 3>(a, kw, alds, stream);
+        case 4: case 6: return launch256<2, 4>(a, kw, alds, stream);
+        default: return launch256<2, 2>(a, kw, alds, stream);
       }
     }
     switch (d) {
-      case 2: return launch256<1, 2>(a, kw, stream);
-      case 4: return launch256<1, 4>(a, kw, stream);
-      case 6: return launch256<1, 6>(a, kw, stream);
-      default: return launch256<1, 3>(a, kw, stream);
+      case 2: return launch256<1, 2>(a, kw, alds, stream);
+      case 4: return launch256<1, 4>(a, kw, alds, stream);
+      case 6: return launch256<1, 6>(a, kw, alds, stream);
+      default: return launch256<1, 3>(a, kw, alds, stream);
     }
   }
   const int vb = (a.K % 32 == 0) ? 2 : 1;

@@ -67,6 +67,26 @@ def test_gemm_small_shapes_all_paths(M, K, N):
                         f"M={M} K={K} N={N} path={path} {out_dtype}")
 
 
+# One or two activation rows with K >= 2048 and K % 256 == 0 take the memory-order GEMV: rows
+# whose chunk count (K/32) is not a multiple of 64, row runs that wrap inside an instruction,
+# several rows per wave (N above the resident wave count), a single row; K = 2080 (odd chunk
+# count, scale rows not 16-byte aligned) is served by the general kernel.
+GEMV_KNS = [(2048, 1), (2080, 64), (2080, 37), (3072, 515), (2304, 3000), (5120, 2600)]
+
+
+@pytest.mark.parametrize("K,N", GEMV_KNS)
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemv_ragged_shapes(M, K, N):
+    rng = np.random.default_rng(7 * M + K + 3 * N)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    dev, ref = _quantized_pair(A, W)
+    C, T = _oracle(ref)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        out = B.nvfp4_gemm(*dev, out_dtype=out_dtype)
+        U.assert_within(U.host(out), C, T + U.out_rounding_slack(C, out_dtype), f"M={M} K={K} N={N} {out_dtype}")
+
+
 def test_gemm_deterministic_and_paths_agree_at_m16():
     rng = np.random.default_rng(5)
     W = (rng.standard_normal((1000, 5120)) * 0.02).astype(np.float32)
