@@ -26,6 +26,7 @@ ARCH = "gfx950"
 SOURCES = {
     "quant.hip": ["-ffp-contract=off"],
     "gemm_skinny.hip": [],
+    "gemv_fp4.hip": [],
     "gemm_tiled.hip": [],
     "abi.cpp": [],
 }

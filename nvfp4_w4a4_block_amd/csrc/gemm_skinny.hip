@@ -918,8 +918,9 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   // f16 activation rows within 64 KiB of LDS).  NVFP4_GEMV=0 disables it;
   // NVFP4_GEMV_G (rows per wave / 4) and NVFP4_GEMV_W (waves per workgroup)
   // are tuning knobs.
-  const int e_gemv = env_int("NVFP4_GEMV", 2);
-  if (e_gemv == 2 && a.M <= 2 && a.K >= 2048 && a.K % 256 == 0) {
+  const int e_gemv = env_int("NVFP4_GEMV", 3);
+  if (e_gemv == 3 && gemv_fp4_supported(a)) return launch_gemv_fp4(a, stream);
+  if (e_gemv >= 2 && a.M <= 2 && a.K >= 2048 && a.K % 256 == 0) {
     int e_w = env_int("NVFP4_GEMV_W", 4);
     if (e_w != 4 && e_w != 8) e_w = 4;
     int R = flat_rows_per_wave(a, e_w, env_int("NVFP4_FLAT_C", 1));

@@ -31,6 +31,11 @@ struct GemmArgs {
 // Weight-streaming path (built for M <= 16; tiles larger M by 16 rows).
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
 
+// FP4 matrix-core GEMV for M <= 2 (K % 256 == 0, K <= 16384 within its LDS
+// budget); launch only where gemv_fp4_supported() holds.
+bool gemv_fp4_supported(const GemmArgs& a);
+hipError_t launch_gemv_fp4(const GemmArgs& a, hipStream_t stream);
+
 // LDS-tiled MFMA path for large M.
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
 
