@@ -132,6 +132,31 @@ nvfp4_status nvfp4_gemm_ex(int64_t M, int64_t K, int64_t N,
                            const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
                            void* out, nvfp4_dtype out_dt, int path, void* stream);
 
+/* Activation quantization and GEMM in one call: the decode step's
+ * nvfp4_quantize_act + nvfp4_gemm.
+ *   a         [M][K] raw activations in a_dt (NVFP4_F32 or NVFP4_BF16), device.
+ *   a_global  in: device float, the static calibrated decode scale g_a.
+ *   w_codes, w_scales, w_global, out, out_dt: as nvfp4_gemm.
+ *   a_codes   out: [M][K/2];  a_scales out: [M][K/16]: the activations' NVFP4
+ *             form, bit-identical to nvfp4_quantize_act; required (they are
+ *             also the intermediate when the call runs as two launches).
+ * out is bit-identical to nvfp4_quantize_act followed by nvfp4_gemm.  For
+ * M <= 2 with K a multiple of 1024 in [1024, 8192] this is one kernel: each
+ * workgroup quantizes the activation rows into its LDS while its first
+ * weight loads are in flight (the standalone quantization launch and its
+ * round trip through memory disappear from the decode step); other shapes run
+ * the two launches.  N == 0 only quantizes.  Validation as nvfp4_gemm, with
+ * a_dt checked with out_dt and a, a_global, a_codes, a_scales always required
+ * for M > 0.
+ * Cites: the page section "Using NVFP4 quantization to accelerate Qwen3.6-27B
+ * inference" (NVFP4 activations shrink the memory traffic of low-batch
+ * decode, which is bandwidth bound). */
+nvfp4_status nvfp4_quantize_gemm(int64_t M, int64_t K, int64_t N,
+                                 const void* a, nvfp4_dtype a_dt, const float* a_global,
+                                 const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                                 void* out, nvfp4_dtype out_dt, uint8_t* a_codes, uint8_t* a_scales,
+                                 void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* nvfp4_status_string(nvfp4_status s);
 

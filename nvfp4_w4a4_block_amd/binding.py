@@ -22,8 +22,8 @@ NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_DTYPE, NVF
 NVFP4_F32, NVFP4_BF16 = 0, 1
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 
-EXPORTS = ("nvfp4_quantize_weights", "nvfp4_quantize_act", "nvfp4_gemm", "nvfp4_gemm_ex",
-           "nvfp4_status_string", "nvfp4_abi_version")
+EXPORTS = ("nvfp4_abi_version", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_quantize_act",
+           "nvfp4_quantize_gemm", "nvfp4_quantize_weights", "nvfp4_status_string")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -47,7 +47,9 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_quantize_act.argtypes = [p, i32, i64, i64, p, p, p, p]
     lib.nvfp4_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, p]
     lib.nvfp4_gemm_ex.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, i32, p]
-    for f in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "nvfp4_gemm", "nvfp4_gemm_ex"):
+    lib.nvfp4_quantize_gemm.argtypes = [i64, i64, i64, p, i32, p, p, p, p, p, i32, p, p, p]
+    for f in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "nvfp4_gemm", "nvfp4_gemm_ex",
+              "nvfp4_quantize_gemm"):
         getattr(lib, f).restype = i32
     lib.nvfp4_status_string.argtypes = [i32]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
@@ -155,3 +157,42 @@ def nvfp4_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: torch.Tensor,
                                 out.data_ptr(), _dt(out_dtype), path, _stream(dev)),
            "nvfp4_gemm")
     return out
+
+
+def nvfp4_quantize_gemm(a: torch.Tensor, g_a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
+                        g_w: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                        out: Optional[torch.Tensor] = None, a_codes: Optional[torch.Tensor] = None,
+                        a_scales: Optional[torch.Tensor] = None
+                        ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Raw activations a [M, K] (float32/bfloat16) with device scale g_a [1] times the NVFP4
+    weights: returns (out [M, N], a_codes [M, K/2], a_scales [M, K/16])."""
+    if a.dim() != 2 or w_codes.dim() != 2:
+        raise ValueError("a and w_codes must be 2-D")
+    M, K = a.shape
+    N = w_codes.shape[0]
+    if w_codes.shape[1] != K // 2 or w_scales.shape != (N, K // 16):
+        raise ValueError("inconsistent operand shapes")
+    if w_codes.dtype != torch.uint8 or w_scales.dtype != torch.uint8:
+        raise ValueError("codes and scales must be uint8")
+    for g in (g_a, g_w):
+        if g.dtype != torch.float32 or g.numel() != 1:
+            raise ValueError("tensor scales must be float32 tensors of one element")
+    dev = _dev(a, g_a, w_codes, w_scales, g_w)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    elif out.shape != (M, N) or out.dtype != out_dtype:
+        raise ValueError("out must be [M, N] of out_dtype")
+    if a_codes is None:
+        a_codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if a_scales is None:
+        a_scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    if a_codes.dtype != torch.uint8 or a_scales.dtype != torch.uint8 or \
+            a_codes.numel() != M * (K // 2) or a_scales.numel() != M * (K // 16):
+        raise ValueError("a_codes/a_scales must be uint8 of [M, K/2] / [M, K/16] elements")
+    _dev(a, out, a_codes, a_scales)
+    _check(load().nvfp4_quantize_gemm(M, K, N, a.data_ptr(), _dt(a.dtype), g_a.data_ptr(),
+                                      w_codes.data_ptr(), w_scales.data_ptr(), g_w.data_ptr(),
+                                      out.data_ptr(), _dt(out_dtype), a_codes.data_ptr(),
+                                      a_scales.data_ptr(), _stream(dev)),
+           "nvfp4_quantize_gemm")
+    return out, a_codes, a_scales

@@ -57,6 +57,31 @@ __device__ __forceinline__ uint32_t e2m1_from_f32(float y) {
 
 // ---------------------------------------------------------------------------
 // Dequantization to MFMA operands.
+// One 16-block x[0..15] with decode scale g -> its E4M3 scale byte (returned)
+// and 16 E2M1 codes in two words (element 2j in the low nibble of byte j).
+// The same fp32 sequence as every quantizer in this library: amax, s =
+// (amax / 6) / g, scale byte, d = sv * g, inv = 1 / d, codes of x_i * inv.
+// Each step is one correctly rounded operation (the library is built with
+// correctly rounded division); there is no sum, so nothing can be contracted
+// into a fused multiply-add.
+__device__ __forceinline__ uint32_t quantize_block16(const float* x, float g, uint32_t& w0, uint32_t& w1) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+  const float s = (g == 0.0f) ? 0.0f : (amax / 6.0f) / g;
+  const uint32_t sb = e4m3_from_nonneg(s);
+  const float d = e4m3_to_f32(sb) * g;
+  const float inv = (d == 0.0f) ? 0.0f : 1.0f / d;
+  w0 = 0u;
+  w1 = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    w0 |= e2m1_from_f32(x[i] * inv) << (4 * i);
+    w1 |= e2m1_from_f32(x[8 + i] * inv) << (4 * i);
+  }
+  return sb;
+}
+
 // ---------------------------------------------------------------------------
 
 // Two E4M3 scale bytes (low two bytes of `w`) -> f16 pair, exact: every E4M3

@@ -66,7 +66,12 @@ size_t fp4_lds_bytes(int MR, int K, int G) {
 // a line costs one weight load, three LDS reads, one MFMA per activation row
 // and the scale arithmetic.  D weight loads are in flight per wave (D divides
 // L, so ring slots are static across groups).
-template <int MR, int L, int D, bool OUT_BF16>
+//
+// FUSE = 0 reads pre-quantized activation codes and scales; FUSE = 1 (bf16)
+// or 2 (fp32) reads the raw activation rows and quantizes their 16-blocks in
+// the set-up (quantize_block16, bit-identical to the activation quantizer),
+// every workgroup for itself; workgroup 0 also stores the codes and scales.
+template <int MR, int L, int D, bool OUT_BF16, int FUSE>
 __global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
   static_assert(L % D == 0 && D <= L, "ring depth must divide the line count");
   constexpr int K = 256 * L;
@@ -100,17 +105,37 @@ __global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
   // lane i + 16g of line t carries block i's 8 code bytes when g == (i%8)/2.
   const int ti = lane & 15, tg = lane >> 4;
   const bool nz = tg == ((ti & 7) >> 1);
-  u2_t fa[kFillPerThread];
-#pragma unroll
-  for (int s = 0; s < kFillPerThread; ++s) {
-    const int tau = wave + kWaves * s;
-    const int m = tau >= L ? 1 : 0;
-    const int t = tau - m * L;
-    const bool ok = nz && tau < MR * L;
-    fa[s] = __builtin_amdgcn_raw_buffer_load_b64(ac, ok ? m * row_bytes + (16u * t + ti) * 8u : kOOB, 0, 0);
-  }
+  constexpr int kFillLoads = FUSE == 0 ? kFillPerThread : 1;
+  u2_t fa[kFillLoads];
+  uint32_t asb = 0;
   const uint32_t a_dw = (uint32_t)threadIdx.x;  // activation scales, 4 bytes per thread
-  const uint32_t asb = __builtin_amdgcn_raw_buffer_load_b32(as, a_dw * 4u < MR * srow ? a_dw * 4u : kOOB, 0, 0);
+  // Fused: 16-blocks tid, tid + 256, ... of the raw rows, 16-byte pieces.
+  constexpr int kRawBlocks = MR * L * 16;
+  constexpr int kRawPerThread = (kRawBlocks + 255) / 256;
+  constexpr int kRawVec = FUSE == 2 ? 4 : 2;  // 16-byte loads per block (fp32 : bf16)
+  u4_t xr[FUSE == 0 ? 1 : kRawPerThread][kRawVec];
+  if constexpr (FUSE == 0) {
+#pragma unroll
+    for (int s = 0; s < kFillPerThread; ++s) {
+      const int tau = wave + kWaves * s;
+      const int m = tau >= L ? 1 : 0;
+      const int t = tau - m * L;
+      const bool ok = nz && tau < MR * L;
+      fa[s] = __builtin_amdgcn_raw_buffer_load_b64(ac, ok ? m * row_bytes + (16u * t + ti) * 8u : kOOB, 0, 0);
+    }
+    asb = __builtin_amdgcn_raw_buffer_load_b32(as, a_dw * 4u < MR * srow ? a_dw * 4u : kOOB, 0, 0);
+  } else {
+    const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(p.a_raw), (short)0, (int)(kRawBlocks * 16 * kRawVec), 0x00020000);
+#pragma unroll
+    for (int s = 0; s < kRawPerThread; ++s) {
+      const uint32_t b = threadIdx.x + 256u * s;
+#pragma unroll
+      for (int v = 0; v < kRawVec; ++v)
+        xr[s][v] = __builtin_amdgcn_raw_buffer_load_b128(ar, b < (uint32_t)kRawBlocks ? (b * kRawVec + v) * 16u : kOOB,
+                                                          0, 0);
+    }
+  }
   // This wave's weight scales: rows row0 .. row0 + 8G - 1, contiguous.
   u4_t sreg[kScaleLoads];
 #pragma unroll
@@ -139,16 +164,55 @@ __global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
   }
 
   // ---- set-up stores (wait for the set-up loads only) ----
+  if constexpr (FUSE == 0) {
 #pragma unroll
-  for (int s = 0; s < kFillPerThread; ++s) {
-    const int tau = wave + kWaves * s;
-    if (tau < MR * L)
-      tiles[tau * 64 + lane] = (ti & 1) ? u4_t{0u, 0u, fa[s].x, fa[s].y} : u4_t{fa[s].x, fa[s].y, 0u, 0u};
-  }
-  if (a_dw * 4u < MR * srow) {
-    const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(asb, false);
-    const f2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(asb, true);
-    *reinterpret_cast<f4_t*>(asc + 4 * a_dw) = f4_t{lo.x, lo.y, hi.x, hi.y};
+    for (int s = 0; s < kFillPerThread; ++s) {
+      const int tau = wave + kWaves * s;
+      if (tau < MR * L)
+        tiles[tau * 64 + lane] = (ti & 1) ? u4_t{0u, 0u, fa[s].x, fa[s].y} : u4_t{fa[s].x, fa[s].y, 0u, 0u};
+    }
+    if (a_dw * 4u < MR * srow) {
+      const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(asb, false);
+      const f2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(asb, true);
+      *reinterpret_cast<f4_t*>(asc + 4 * a_dw) = f4_t{lo.x, lo.y, hi.x, hi.y};
+    }
+  } else {
+    const float ga = *p.ga;
+#pragma unroll
+    for (int s = 0; s < kRawPerThread; ++s) {
+      const uint32_t b = threadIdx.x + 256u * s;
+      if (b < (uint32_t)kRawBlocks) {
+        float x[16];
+#pragma unroll
+        for (int v = 0; v < kRawVec; ++v)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t w = xr[s][v][c];
+            if constexpr (FUSE == 2) {
+              x[4 * v + c] = __builtin_bit_cast(float, w);
+            } else {  // two bf16: element 2c in the low half
+              x[8 * v + 2 * c] = __builtin_bit_cast(float, w << 16);
+              x[8 * v + 2 * c + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
+            }
+          }
+        uint32_t w0, w1;
+        const uint32_t sb = quantize_block16(x, ga, w0, w1);
+        const uint32_t m = b >= 16u * L ? 1u : 0u;
+        const uint32_t blk = b - m * 16u * L;  // block within the row
+        const uint32_t t = blk >> 4, i = blk & 15;
+        u4_t* e = tiles + (m * L + t) * 64 + i;
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg)
+          e[16 * gg] = gg != (int)((i & 7) >> 1) ? u4_t{0u, 0u, 0u, 0u}
+                       : (i & 1)                 ? u4_t{0u, 0u, w0, w1}
+                                                 : u4_t{w0, w1, 0u, 0u};
+        asc[m * (K >> 4) + blk] = e4m3_to_f32(sb);
+        if (blockIdx.x == 0) {
+          *reinterpret_cast<u2_t*>(p.ac_out + m * (K >> 1) + blk * 8) = u2_t{w0, w1};
+          p.as_out[m * (K >> 4) + blk] = (uint8_t)sb;
+        }
+      }
+    }
   }
 #pragma unroll
   for (int s = 0; s < kScaleLoads; ++s) {
@@ -268,14 +332,20 @@ int device_cus() {
   return cus[dev];
 }
 
-template <int MR, int L, int D>
+template <int MR, int L, int D, int FUSE>
 hipError_t launch_fp4(const GemmArgs& a, int G, hipStream_t stream) {
   const int64_t waves = (a.N + 8 * G - 1) / (8 * G);
   const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
   const size_t lds = fp4_lds_bytes(MR, a.K, G);
-  if (a.out_bf16) gemv_fp4_kernel<MR, L, D, true><<<grid, 64 * kWaves, lds, stream>>>(a, G);
-  else gemv_fp4_kernel<MR, L, D, false><<<grid, 64 * kWaves, lds, stream>>>(a, G);
+  if (a.out_bf16) gemv_fp4_kernel<MR, L, D, true, FUSE><<<grid, 64 * kWaves, lds, stream>>>(a, G);
+  else gemv_fp4_kernel<MR, L, D, false, FUSE><<<grid, 64 * kWaves, lds, stream>>>(a, G);
   return hipGetLastError();
+}
+
+template <int MR, int L, int D>
+hipError_t launch_fp4(const GemmArgs& a, int G, hipStream_t stream) {
+  if (!a.a_raw) return launch_fp4<MR, L, D, 0>(a, G, stream);
+  return a.a_raw_bf16 ? launch_fp4<MR, L, D, 1>(a, G, stream) : launch_fp4<MR, L, D, 2>(a, G, stream);
 }
 
 template <int MR>

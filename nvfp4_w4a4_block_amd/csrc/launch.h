@@ -26,6 +26,13 @@ struct GemmArgs {
   const float* gw;    // weight decode scale (device)
   void* out;          // [M][N]
   bool out_bf16;
+  // Fused activation quantization (FP4 GEMV only): when a_raw is set, the
+  // kernel quantizes the [M][K] activation rows itself with *ga and writes
+  // their codes and scales to ac_out / as_out; ac and as are then unused.
+  const void* a_raw = nullptr;
+  bool a_raw_bf16 = false;
+  uint8_t* ac_out = nullptr;
+  uint8_t* as_out = nullptr;
 };
 
 // Weight-streaming path (built for M <= 16; tiles larger M by 16 rows).

@@ -1,0 +1,121 @@
+"""Summaries of rocprofv3 runs of bench.py, as committed under profiles/.
+
+    python -m nvfp4_w4a4_block_amd.profile_summary trace <kernel_stats.csv> <out.md> \
+        --title TEXT --command TEXT [--bytes B --kernel SUBSTR]
+    python -m nvfp4_w4a4_block_amd.profile_summary traffic <fetch.csv> <write.csv> <out.json> \
+        --kernel SUBSTR --sources FILE... --command TEXT --command TEXT [--copy-mib 128]
+
+`trace` turns the per-kernel statistics of `rocprofv3 --kernel-trace --stats
+--output-format csv` into a markdown table (and, with --bytes, the achieved
+GB/s of the named kernel).  `traffic` reads two `rocprofv3 --pmc FETCH_SIZE`
+/ `--pmc WRITE_SIZE` counter files of a bench run made with
+--copy-reference-mib, scales each counter by what it reads for that plain copy
+of known size (the last three copy dispatches), and writes the HBM bytes per
+launch of the named kernel together with a SHA-256 of the kernel's sources;
+bench.py reports the figure only while those sources are unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def sources_sha256(sources) -> str:
+    h = hashlib.sha256()
+    for src in sources:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def trace(args) -> None:
+    rows = list(csv.DictReader(open(args.stats)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = [f"# {args.title}", "", "Command (repository root, MI355X):", "", "```", args.command, "```", ""]
+    if args.bytes and args.kernel:
+        k = [r for r in rows if args.kernel in r["Name"]]
+        if k:
+            avg = float(k[0]["AverageNs"])
+            out += [f"Algorithmic bytes per launch of `{args.kernel}`: {args.bytes:,}; "
+                    f"average {avg:,.1f} ns -> {args.bytes / avg:,.1f} GB/s "
+                    f"({100 * args.bytes / avg / 8000:.1f}% of 8 TB/s).", ""]
+    out += ["| Name | Calls | Total (ns) | Average (ns) | Percent | Min (ns) | Max (ns) |",
+            "| :-- | --: | --: | --: | --: | --: | --: |"]
+    for r in rows:
+        out.append(f"| {r['Name'][:150]} | {r['Calls']} | {float(r['TotalDurationNs']):.0f} | "
+                   f"{float(r['AverageNs']):.1f} | {float(r['Percentage']):.2f} | {float(r['MinNs']):.0f} | "
+                   f"{float(r['MaxNs']):.0f} |")
+    with open(args.out, "w") as f:
+        f.write("\n".join(out) + "\n")
+
+
+def _per_kernel(path: str, counter: str):
+    """Counter values (KiB per dispatch) grouped as (kernel dispatches, copy dispatches)."""
+    recs = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    recs.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return recs
+
+
+def traffic(args) -> None:
+    res = {}
+    for counter, path in (("FETCH_SIZE", args.fetch), ("WRITE_SIZE", args.write)):
+        recs = _per_kernel(path, counter)
+        kern = [float(r["Counter_Value"]) for r in recs if args.kernel in r["Kernel_Name"]]
+        copies = [float(r["Counter_Value"]) for r in recs if "copyBuffer" in r["Kernel_Name"]][-3:]
+        if not kern or len(copies) < 3:
+            sys.exit(f"{path}: {len(kern)} dispatches of {args.kernel!r}, {len(copies)} reference copies")
+        res[counter] = (statistics.mean(kern), statistics.mean(copies), len(kern))
+    ref_kib = args.copy_mib * 1024.0
+    f_kib, f_ref, n = res["FETCH_SIZE"]
+    w_kib, w_ref, _ = res["WRITE_SIZE"]
+    f_scale, w_scale = ref_kib / f_ref, ref_kib / w_ref
+    rec = {
+        "kernel": args.kernel,
+        "sources": args.sources,
+        "sources_sha256": sources_sha256(args.sources),
+        "dispatches": n,
+        "fetch_size_kib_per_dispatch": round(f_kib, 1),
+        "write_size_kib_per_dispatch": round(w_kib, 1),
+        "copy_reference": f"device copy of {args.copy_mib} MiB: FETCH_SIZE {f_ref:.1f} KiB, "
+                          f"WRITE_SIZE {w_ref:.1f} KiB",
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "traffic_bytes_per_launch": int(round((f_kib * f_scale + w_kib * w_scale) * 1024)),
+        "commands": args.command,
+    }
+    with open(args.out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("stats")
+    t.add_argument("out")
+    t.add_argument("--title", required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--bytes", type=int, default=0)
+    t.add_argument("--kernel", default="")
+    r = sub.add_parser("traffic")
+    r.add_argument("fetch")
+    r.add_argument("write")
+    r.add_argument("out")
+    r.add_argument("--kernel", required=True)
+    r.add_argument("--sources", nargs="+", required=True)
+    r.add_argument("--command", action="append", required=True)
+    r.add_argument("--copy-mib", type=int, default=128)
+    a = ap.parse_args()
+    trace(a) if a.cmd == "trace" else traffic(a)
+
+
+if __name__ == "__main__":
+    main()
