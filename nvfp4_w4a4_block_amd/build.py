@@ -27,6 +27,7 @@ SOURCES = {
     "quant.hip": ["-ffp-contract=off"],
     "gemm_skinny.hip": [],
     "gemv_fp4.hip": [],
+    "gemm_m16.hip": [],
     "gemm_tiled.hip": [],
     "abi.cpp": [],
 }

@@ -43,6 +43,10 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
 bool gemv_fp4_supported(const GemmArgs& a);
 hipError_t launch_gemv_fp4(const GemmArgs& a, hipStream_t stream);
 
+// Weight-streaming GEMM for M <= 16 on f16 matrix cores (K % 256 == 0).
+bool gemm_m16_supported(const GemmArgs& a);
+hipError_t launch_gemm_m16(const GemmArgs& a, hipStream_t stream);
+
 // LDS-tiled MFMA path for large M.
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
 
