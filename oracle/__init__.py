@@ -14,7 +14,10 @@ nearest-value search, and multiplies dense dequantized matrices in fp64.
 
 Pinned by tests/test_oracle_*.py against closed forms, torch's float8_e4m3fn
 casts, hand-worked blocks (tests/golden/) and exact rational brute force.
+`tree` adds the greedy verification of a candidate tree over the LM head
+(section "Using tree-based multi-token prediction to accelerate LLM
+inference"), pinned by hand-worked trees and an exhaustive path search.
 Parity unpinned by the pages themselves: the per-tensor scale formula
 amax/(6*448) and the static activation scale are readings, not page facts.
 """
-from . import formats, quant, gemm  # noqa: F401
+from . import formats, quant, gemm, tree  # noqa: F401
