@@ -92,6 +92,16 @@ class Pipeline:
         self.as1 = torch.empty((M, K // 16), dtype=torch.uint8, device=DEV)
         self.out_dtype = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
         self.y1 = torch.empty((M, N), dtype=self.out_dtype, device=DEV)
+        self.tree = wl.name == "tree_verify"
+        if self.tree:  # 16 nodes over 8 depths: a main chain plus one alternative per depth
+            parent, chain = [-1], [0]
+            for _ in range(7):
+                parent += [chain[-1], chain[-1]]
+                chain.append(len(parent) - 2)
+            parent.append(chain[-1])
+            self.parent = torch.tensor(parent, dtype=torch.int32, device=DEV)
+            self.draft = torch.zeros(M, dtype=torch.int32, device=DEV)
+            B.nvfp4_quantize_act(self.a, self.g1, self.ac1, self.as1)
         if wl.chain:
             self.ac2 = torch.empty((M, N // 2), dtype=torch.uint8, device=DEV)
             self.as2 = torch.empty((M, N // 16), dtype=torch.uint8, device=DEV)
@@ -107,7 +117,17 @@ class Pipeline:
         B.nvfp4_quantize_gemm(self.a, self.g1, wc, ws, gw, out_dtype=self.out_dtype, out=self.y1,
                               a_codes=self.ac1, a_scales=self.as1)
 
+    def _verify(self, i):
+        """Tree verification: quantize the 16 node rows, then LM head + fused argmax + greedy
+        acceptance (nvfp4_tree_verify, three launches, no logits written)."""
+        wc, ws, gw = self.l1.copies[i % self.R]
+        B.nvfp4_tree_verify(self.ac1, self.as1, self.g1, wc, ws, gw, self.parent, self.draft)
+
     def step(self, i):
+        if self.tree:
+            B.nvfp4_quantize_act(self.a, self.g1, self.ac1, self.as1)
+            self._verify(i)
+            return
         self._gemm1(i)
         if self.l2 is not None:
             wc, ws, gw = self.l2.copies[i % self.R]
@@ -124,6 +144,9 @@ class Pipeline:
     def gemm_only(self, i):
         """The dominant kernel alone, for its per-launch duration: the fused kernel where the
         step is one kernel, else the first GEMM on already quantized activations."""
+        if self.tree:
+            self._verify(i)
+            return
         if self.fused_single_kernel:
             self._gemm1(i)
             return
@@ -248,7 +271,8 @@ def main() -> int:
     torch.cuda.synchronize()
     step_ms = timed_replays(step_graphs, K, P.R) / K
     kern_ms = timed_replays(gemm_graphs, K, P.R) / K
-    kname = "fused quantize + FP4 GEMV" if P.fused_single_kernel else "first GEMM"
+    kname = ("LM head + fused argmax + tree acceptance" if P.tree else
+             "fused quantize + FP4 GEMV" if P.fused_single_kernel else "first GEMM")
     log(f"[bench] step {step_ms * 1e3:.2f} us, {kname} {kern_ms * 1e3:.2f} us per launch")
 
     if wl.chain:

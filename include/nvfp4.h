@@ -157,6 +157,48 @@ nvfp4_status nvfp4_quantize_gemm(int64_t M, int64_t K, int64_t N,
                                  void* out, nvfp4_dtype out_dt, uint8_t* a_codes, uint8_t* a_scales,
                                  void* stream);
 
+/* Greedy (temperature-0) acceptance of a verified candidate tree.
+ *   n_nodes  1..64 tree nodes in topological order; node 0 is the root.
+ *   parent   [n_nodes] int32, device: parent[0] = -1, 0 <= parent[v] < v
+ *            (an index outside [0, v) rejects node v).
+ *   draft    [n_nodes] int32, device: node v's drafted token (entry 0 unused).
+ *   greedy   [n_nodes] int32, device: the target's argmax token after node v.
+ *   result   out [3 + n_nodes] int32, device: end node, accepted draft count L,
+ *            bonus token, then the L accepted nodes root-child first, then -1.
+ * Node v is accepted when its parent is and draft[v] == greedy[parent[v]];
+ * the path ends at the deepest accepted node (lowest index on ties) and the
+ * bonus token is greedy[end]: one verification advances L + 1 tokens.
+ * Cites: the page section "Using tree-based multi-token prediction to
+ * accelerate LLM inference" (one forward pass verifies the tree; the
+ * matching path is accepted) and the benchmark's temperature 0. */
+nvfp4_status nvfp4_tree_accept(int64_t n_nodes, const int32_t* parent, const int32_t* draft, const int32_t* greedy,
+                               int32_t* result, void* stream);
+
+/* LM head over a candidate tree plus greedy acceptance, in one call.
+ *   M        1..16 tree nodes (rows); K, N (vocabulary): as nvfp4_gemm, with the
+ *            nodes' NVFP4 activations a_* and the LM-head weights w_*.
+ *   parent, draft: as nvfp4_tree_accept.
+ *   logits   optional out [M][N] fp32 (may be NULL when K % 256 == 0 and
+ *            K <= 5120: the argmax is then fused into the GEMM and the logits
+ *            are not written; other K need it).
+ *   greedy   out [M] int32: each row's argmax (lowest column on ties; -0.0
+ *            orders just below +0.0).
+ *   result   out [3 + M] int32: as nvfp4_tree_accept.
+ *   keys     workspace of 1024 64-bit words (8 KiB), device, 8-byte aligned,
+ *            caller-owned: must be all zero on entry and is all zero again on
+ *            return (clear it once before first use; calls sharing it must be
+ *            stream-ordered).
+ * Deterministic: the argmax merges per-workgroup maxima with atomic maxima
+ * (64 slots per row, folded by the acceptance kernel), whose result does not
+ * depend on their order.
+ * Cites: the sections on tree-based multi-token prediction (16-node tree
+ * verified in one pass) and NVFP4 quantization (the LM head is NVFP4). */
+nvfp4_status nvfp4_tree_verify(int64_t M, int64_t K, int64_t N,
+                               const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                               const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                               const int32_t* parent, const int32_t* draft, float* logits, int32_t* greedy,
+                               int32_t* result, uint64_t* keys, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* nvfp4_status_string(nvfp4_status s);
 

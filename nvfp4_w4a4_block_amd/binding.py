@@ -23,7 +23,8 @@ NVFP4_F32, NVFP4_BF16 = 0, 1
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 
 EXPORTS = ("nvfp4_abi_version", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_quantize_act",
-           "nvfp4_quantize_gemm", "nvfp4_quantize_weights", "nvfp4_status_string")
+           "nvfp4_quantize_gemm", "nvfp4_quantize_weights", "nvfp4_status_string", "nvfp4_tree_accept",
+           "nvfp4_tree_verify")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -48,8 +49,10 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, p]
     lib.nvfp4_gemm_ex.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, i32, p]
     lib.nvfp4_quantize_gemm.argtypes = [i64, i64, i64, p, i32, p, p, p, p, p, i32, p, p, p]
+    lib.nvfp4_tree_accept.argtypes = [i64, p, p, p, p, p]
+    lib.nvfp4_tree_verify.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p, p, p, p, p, p]
     for f in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "nvfp4_gemm", "nvfp4_gemm_ex",
-              "nvfp4_quantize_gemm"):
+              "nvfp4_quantize_gemm", "nvfp4_tree_accept", "nvfp4_tree_verify"):
         getattr(lib, f).restype = i32
     lib.nvfp4_status_string.argtypes = [i32]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
@@ -196,3 +199,64 @@ def nvfp4_quantize_gemm(a: torch.Tensor, g_a: torch.Tensor, w_codes: torch.Tenso
                                       a_scales.data_ptr(), _stream(dev)),
            "nvfp4_quantize_gemm")
     return out, a_codes, a_scales
+
+
+def _int32_vec(t: torch.Tensor, n: int, name: str) -> None:
+    if t.dtype != torch.int32 or t.dim() != 1 or t.numel() != n:
+        raise ValueError(f"{name} must be an int32 vector of {n} elements")
+
+
+def nvfp4_tree_accept(parent: torch.Tensor, draft: torch.Tensor, greedy: torch.Tensor) -> torch.Tensor:
+    """Greedy acceptance of a candidate tree: returns result int32 [3 + n] = (end node, accepted
+    count L, bonus token, L path nodes, -1 padding)."""
+    n = parent.numel()
+    for t, name in ((parent, "parent"), (draft, "draft"), (greedy, "greedy")):
+        _int32_vec(t, n, name)
+    dev = _dev(parent, draft, greedy)
+    result = torch.empty((3 + n,), dtype=torch.int32, device=dev)
+    _check(load().nvfp4_tree_accept(n, parent.data_ptr(), draft.data_ptr(), greedy.data_ptr(),
+                                    result.data_ptr(), _stream(dev)), "nvfp4_tree_accept")
+    return result
+
+
+_key_workspaces: dict = {}
+
+
+def tree_key_workspace(dev: torch.device) -> torch.Tensor:
+    """The argmax-key workspace of nvfp4_tree_verify for `dev` (1024 int64, zeroed once; every
+    call leaves it zeroed).  Shared by the calls of this module: keep them on one stream, or
+    pass a workspace of your own."""
+    ws = _key_workspaces.get(dev)
+    if ws is None:
+        ws = _key_workspaces[dev] = torch.zeros((1024,), dtype=torch.int64, device=dev)
+    return ws
+
+
+def nvfp4_tree_verify(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: torch.Tensor,
+                      w_codes: torch.Tensor, w_scales: torch.Tensor, g_w: torch.Tensor,
+                      parent: torch.Tensor, draft: torch.Tensor, want_logits: bool = False,
+                      keys: Optional[torch.Tensor] = None):
+    """LM head over the M tree nodes plus greedy acceptance: returns (greedy int32 [M],
+    result int32 [3 + M], logits fp32 [M, N] or None)."""
+    M, K2 = a_codes.shape
+    N = w_codes.shape[0]
+    K = 2 * K2
+    if w_codes.shape[1] != K2 or a_scales.shape != (M, K // 16) or w_scales.shape != (N, K // 16):
+        raise ValueError("inconsistent operand shapes")
+    _int32_vec(parent, M, "parent")
+    _int32_vec(draft, M, "draft")
+    dev = _dev(a_codes, a_scales, g_a, w_codes, w_scales, g_w, parent, draft)
+    greedy = torch.empty((M,), dtype=torch.int32, device=dev)
+    result = torch.empty((3 + M,), dtype=torch.int32, device=dev)
+    if keys is None:
+        keys = tree_key_workspace(dev)
+    elif keys.dtype != torch.int64 or keys.numel() != 1024 or keys.device != dev:
+        raise ValueError("keys must be 1024 int64 on the operands' device, zero on entry")
+    logits = torch.empty((M, N), dtype=torch.float32, device=dev) if want_logits else None
+    _check(load().nvfp4_tree_verify(M, K, N, a_codes.data_ptr(), a_scales.data_ptr(), g_a.data_ptr(),
+                                    w_codes.data_ptr(), w_scales.data_ptr(), g_w.data_ptr(),
+                                    parent.data_ptr(), draft.data_ptr(),
+                                    logits.data_ptr() if logits is not None else None,
+                                    greedy.data_ptr(), result.data_ptr(), keys.data_ptr(), _stream(dev)),
+           "nvfp4_tree_verify")
+    return greedy, result, logits

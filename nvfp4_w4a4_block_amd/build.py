@@ -28,6 +28,7 @@ SOURCES = {
     "gemm_skinny.hip": [],
     "gemv_fp4.hip": [],
     "gemm_m16.hip": [],
+    "tree.hip": [],
     "gemm_tiled.hip": [],
     "abi.cpp": [],
 }

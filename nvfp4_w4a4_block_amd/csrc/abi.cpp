@@ -41,7 +41,7 @@ const char* nvfp4_status_string(nvfp4_status s) {
   return "unknown status";
 }
 
-int nvfp4_abi_version(void) { return 2; }
+int nvfp4_abi_version(void) { return 3; }
 
 nvfp4_status nvfp4_quantize_weights(const void* w, nvfp4_dtype w_dt, int64_t N, int64_t K,
                                     uint8_t* w_codes, uint8_t* w_scales, float* w_global,
@@ -148,6 +148,55 @@ nvfp4_status nvfp4_quantize_gemm(int64_t M, int64_t K, int64_t N,
   hipError_t e = nvfp4::launch_quantize(a, a_dt == NVFP4_BF16, M, K, a_global, a_codes, a_scales, s);
   if (e != hipSuccess || N == 0) return from_hip(e);
   return from_hip(M <= 16 ? nvfp4::launch_gemm_skinny(g, s) : nvfp4::launch_gemm_tiled(g, s));
+}
+
+nvfp4_status nvfp4_tree_accept(int64_t n_nodes, const int32_t* parent, const int32_t* draft, const int32_t* greedy,
+                               int32_t* result, void* stream) {
+  if (n_nodes < 1 || n_nodes > 64) return NVFP4_ERR_SHAPE;
+  if (!parent || !draft || !greedy || !result) return NVFP4_ERR_NULL;
+  if (!aligned4(parent) || !aligned4(draft) || !aligned4(greedy) || !aligned4(result)) return NVFP4_ERR_ALIGN;
+  return from_hip(nvfp4::launch_tree_accept((int)n_nodes, parent, draft, greedy, nullptr, nullptr, result,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_tree_verify(int64_t M, int64_t K, int64_t N,
+                               const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                               const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                               const int32_t* parent, const int32_t* draft, float* logits, int32_t* greedy,
+                               int32_t* result, uint64_t* keys, void* stream) {
+  if (M < 1 || M > 16 || N < 1 || !shape_ok(M, K) || !shape_ok(N, K) || N >= kMaxElems / M) return NVFP4_ERR_SHAPE;
+  if (!a_codes || !a_scales || !a_global || !w_codes || !w_scales || !w_global || !parent || !draft || !greedy ||
+      !result || !keys)
+    return NVFP4_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned4(a_global) || !aligned4(w_global) || !aligned4(parent) || !aligned4(draft) || !aligned4(greedy) ||
+      !aligned4(result) || ((uintptr_t)keys & 7u) != 0 || (logits && !aligned16(logits)))
+    return NVFP4_ERR_ALIGN;
+  nvfp4::GemmArgs g;
+  g.M = (int)M;
+  g.K = (int)K;
+  g.N = (int)N;
+  g.ac = a_codes;
+  g.as = a_scales;
+  g.ga = a_global;
+  g.wc = w_codes;
+  g.ws = w_scales;
+  g.gw = w_global;
+  g.out = logits;
+  g.out_bf16 = false;
+  const bool fused = nvfp4::gemm_m16_supported(g);
+  if (!fused && !logits) return NVFP4_ERR_NULL;  // the unfused form needs the logits
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (fused) {
+    g.argmax_keys = keys;
+    e = nvfp4::launch_gemm_m16(g, s);
+  } else {
+    e = nvfp4::launch_gemm_skinny(g, s);
+    if (e == hipSuccess) e = nvfp4::launch_argmax_rows(logits, (int)M, (int)N, keys, s);
+  }
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(nvfp4::launch_tree_accept((int)M, parent, draft, nullptr, keys, greedy, result, s));
 }
 
 nvfp4_status nvfp4_gemm(int64_t M, int64_t K, int64_t N,

@@ -112,6 +112,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
 }
 
+// Argmax key of logit v at column n: the float's bits mapped to an unsigned
+// order (negative values below positive ones, -0 just below +0) in the high
+// word and the complement of n in the low word, so that the maximum key is the
+// largest value at its lowest column.  Keys of finite values are never 0.
+__device__ __forceinline__ uint64_t argmax_key(float v, uint32_t n) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - n);
+}
+
 __device__ __forceinline__ f4_t mfma16x16x32(h8_t a, h8_t b, f4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

@@ -196,6 +196,9 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
   __syncthreads();
   if (kc != 0) return;
   const float gscale = (*p.ga) * (*p.gw);
+  // With argmax keys, each lane keeps the best (value, column) of its
+  // activation row m = lane % 16 (idx steps by 64, so m is fixed per lane).
+  uint64_t best = 0;
   for (int idx = lane; idx < G * 128; idx += 64) {
     const int g = idx >> 7, r = (idx >> 4) & 7, m = idx & 15;
     float s = 0.f;
@@ -203,13 +206,31 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
     const uint32_t n = row0 + 8u * g + r;
     if (n < (uint32_t)N && m < M) {
       const float v = s * gscale;
-      const int64_t o = (int64_t)m * N + n;
-      if constexpr (OUT_BF16) {
-        reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(v);
-      } else {
-        reinterpret_cast<float*>(p.out)[o] = v;
+      if (p.argmax_keys) {
+        const uint64_t key = argmax_key(v, n);
+        best = key > best ? key : best;
+      }
+      if (p.out) {
+        const int64_t o = (int64_t)m * N + n;
+        if constexpr (OUT_BF16) {
+          reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(v);
+        } else {
+          reinterpret_cast<float*>(p.out)[o] = v;
+        }
       }
     }
+  }
+  if (p.argmax_keys) {
+    // lanes m, m + 16, m + 32, m + 48 share row m; the maximum key is
+    // independent of the order in which the workgroups merge theirs.
+    uint64_t o = __shfl_xor(best, 16);
+    best = o > best ? o : best;
+    o = __shfl_xor(best, 32);
+    best = o > best ? o : best;
+    // spread over kKeySlots slots per row to keep same-address atomics few
+    const uint32_t slot = blockIdx.x % kKeySlots;
+    if (lane < M && best != 0)
+      atomicMax(reinterpret_cast<unsigned long long*>(p.argmax_keys) + slot * 16u + lane, best);
   }
 }
 

@@ -33,7 +33,20 @@ struct GemmArgs {
   bool a_raw_bf16 = false;
   uint8_t* ac_out = nullptr;
   uint8_t* as_out = nullptr;
+  // Fused row argmax (gemm_m16 only): when set, each activation row's largest
+  // output (lowest column on ties) is merged by an atomic maximum of
+  // argmax_key() into argmax_keys[slot][m], slot = workgroup % kKeySlots
+  // ([kKeySlots][16] words, zero on entry); out may then be NULL.
+  uint64_t* argmax_keys = nullptr;
 };
+
+constexpr int kKeySlots = 64;  // argmax key slots per row
+
+// Greedy tree verification over the LM head (tree.hip).  The argmax keys
+// ([kKeySlots][16]) are reduced, and reset to zero, by the acceptance kernel.
+hipError_t launch_argmax_rows(const float* logits, int M, int N, uint64_t* keys, hipStream_t stream);
+hipError_t launch_tree_accept(int n, const int32_t* parent, const int32_t* draft, const int32_t* greedy_in,
+                              uint64_t* keys, int32_t* greedy_out, int32_t* result, hipStream_t stream);
 
 // Weight-streaming path (built for M <= 16; tiles larger M by 16 rows).
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);

@@ -68,6 +68,9 @@ WORKLOADS = {
                  note="16-node tree verification pass, FFN down-projection"),
         Workload("lm_head", 16, 5120, 151936, 0.02, "normal", "bf16", "f32",
                  note="LM head over the 16-node verification tree, fp32 logits"),
+        Workload("tree_verify", 16, 5120, 151936, 0.02, "normal", "bf16", "f32",
+                 note="LM head over the 16-node verification tree with fused greedy acceptance "
+                      "(argmax inside the GEMM, no logits written)"),
         Workload("prefill", 512, 5120, 25600, 0.02, "normal_outliers", "bf16", "bf16",
                  outlier_frac=0.005, outlier_gain=20.0, chain=True,
                  note="suffix prefill: up-proj 5120->25600 then down-proj 25600->5120"),

@@ -12,6 +12,9 @@ match exactly.
 
 For each row the file stores the oracle's argmax, the best and second-best
 logits and the tolerance 1e-3 * sum_k |a_hat * w_hat| at the best column.
+A second file, lm_head_admissible.txt, lists per row every column whose exact
+logit lies within the two columns' tolerances of the exact maximum
+(oracle.tree.admissible_argmax): the argmax a correct fp32 product may return.
 Inputs come from the seeded generator; everything else from oracle/.
 
     python tests/golden/make_lm_head_golden.py      (about 3-4 minutes, ~8 GB RAM)
@@ -27,6 +30,7 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
 from nvfp4_w4a4_block_amd import workloads as WL  # noqa: E402
 from oracle import gemm as G  # noqa: E402
 from oracle import quant as Q  # noqa: E402
+from oracle import tree as TR  # noqa: E402
 
 CHUNK = 2048
 
@@ -58,6 +62,15 @@ def main() -> None:
     with open(os.path.join(HERE, "lm_head_argmax.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+    adm = TR.admissible_argmax(C, T)
+    alines = [
+        "# Admissible argmax columns of the NVFP4 LM head (M=16 K=5120 N=151936, seed 0): every column",
+        "# whose oracle logit is within tol[column] + tol[argmax] of the row maximum (make_lm_head_golden.py).",
+        "# row ; columns",
+    ] + [f"{m} ; {' '.join(str(c) for c in sorted(adm[m]))}" for m in range(wl.M)]
+    with open(os.path.join(HERE, "lm_head_admissible.txt"), "w") as f:
+        f.write("\n".join(alines) + "\n")
+    print("\n".join(alines))
 
 
 if __name__ == "__main__":

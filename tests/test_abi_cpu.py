@@ -42,7 +42,7 @@ def test_status_strings_and_version(lib):
     for s in range(6):
         assert B.status_string(s)
     assert B.status_string(99) == "unknown status"
-    assert lib.nvfp4_abi_version() == 2
+    assert lib.nvfp4_abi_version() == 3
 
 
 def gemm(lib, M, K, N, ptrs=(A16,) * 7, out_dt=B.NVFP4_BF16, path=B.PATH_AUTO):
@@ -124,3 +124,27 @@ def test_quantize_gemm_validation(lib):
         assert qgemm(lib, 1, 5120, 64, ptrs=tuple(ptrs)) == B.NVFP4_ERR_NULL, k
         ptrs[k] = A16 + (2 if k in (1, 4) else 8)  # scalars need 4 bytes, arrays 16
         assert qgemm(lib, 1, 5120, 64, ptrs=tuple(ptrs)) == B.NVFP4_ERR_ALIGN, k
+
+
+def test_tree_entry_points_validate(lib):
+    A = A16
+    assert lib.nvfp4_tree_accept(0, A, A, A, A, None) == B.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_tree_accept(65, A, A, A, A, None) == B.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_tree_accept(16, None, A, A, A, None) == B.NVFP4_ERR_NULL
+    assert lib.nvfp4_tree_accept(16, A + 2, A, A, A, None) == B.NVFP4_ERR_ALIGN
+
+    def verify(M, K, N, ptrs=None, logits=A):
+        ptrs = ptrs or (A,) * 6 + (A, A, A, A, A)
+        ac, asc, ga, wc, wsc, gw, par, dr, gr, res, keys = ptrs
+        return lib.nvfp4_tree_verify(M, K, N, ac, asc, ga, wc, wsc, gw, par, dr, logits, gr, res, keys, None)
+    assert verify(0, 5120, 100) == B.NVFP4_ERR_SHAPE
+    assert verify(17, 5120, 100) == B.NVFP4_ERR_SHAPE
+    assert verify(16, 5120, 0) == B.NVFP4_ERR_SHAPE
+    assert verify(16, 24, 100) == B.NVFP4_ERR_SHAPE
+    ptrs = [A] * 11
+    ptrs[10] = A + 4  # keys need 8-byte alignment
+    assert verify(16, 5120, 100, tuple(ptrs)) == B.NVFP4_ERR_ALIGN
+    ptrs[10] = None
+    assert verify(16, 5120, 100, tuple(ptrs)) == B.NVFP4_ERR_NULL
+    # logits may be omitted only where the argmax is fused (K % 256 == 0, K <= 5120)
+    assert verify(16, 1040, 100, logits=None) == B.NVFP4_ERR_NULL

@@ -167,6 +167,16 @@ def _golden_lm_head():
     return rows
 
 
+def _golden_admissible():
+    adm = {}
+    for line in open(os.path.join(GOLDEN, "lm_head_admissible.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        row, cols = line.split(";")
+        adm[int(row)] = {int(c) for c in cols.split()}
+    return [adm[m] for m in range(len(adm))]
+
+
 def test_lm_head_argmax_matches_oracle():
     """Per-row argmax of the full 151936-column NVFP4 LM head equals the oracle's (the tree
     acceptance at temperature 0 compares argmax tokens)."""
@@ -180,11 +190,16 @@ def test_lm_head_argmax_matches_oracle():
     top = torch.argmax(logits, dim=1).cpu().numpy()
     host = logits.cpu().numpy()
     gold = _golden_lm_head()
-    assert len(gold) == wl.M
+    adm = _golden_admissible()
+    assert len(gold) == wl.M == len(adm)
     for m, best, vbest, second, vsecond, tol in gold:
-        assert top[m] == best, (m, int(top[m]), best, float(host[m, top[m]]), vbest, vsecond)
+        # the GPU decides in fp32: any column within the error bounds of the exact maximum is a
+        # correct argmax; where the oracle leaves a single such column it must be that one
+        assert int(top[m]) in adm[m], (m, int(top[m]), sorted(adm[m]), float(host[m, top[m]]), vbest)
+        if len(adm[m]) == 1:
+            assert top[m] == best
         assert abs(host[m, best] - vbest) <= tol
-        print(f"row {m}: argmax {best} margin {vbest - vsecond:.4g} tol {tol:.3g}")
+        print(f"row {m}: argmax {best} margin {vbest - vsecond:.4g} tol {tol:.3g} admissible {len(adm[m])}")
 
 
 def test_prefill_chain_up_then_down():

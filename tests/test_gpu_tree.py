@@ -1,0 +1,166 @@
+"""GPU parity of greedy tree verification (nvfp4_tree_accept, nvfp4_tree_verify) against the oracle.
+
+Page "TensorRT Edge-LLM Completes the MLPerf Edge Agentic Benchmark 6.4x Faster on Jetson AGX
+Thor", section "Using tree-based multi-token prediction to accelerate LLM inference": the target
+verifies a 16-node candidate tree (8 draft steps, top-2 candidates per depth) in one LM-head pass at
+temperature 0 and accepts the matching path.  Acceptance is integer work and must match the oracle
+exactly.  The argmax of a row is decided in fp32 on the GPU; where the oracle's exact logits put
+several columns within the error bound of the maximum, any of them is a correct argmax, so the GPU's
+choice is checked against that admissible set, and drafts never hinge on such a row: a child copies
+its parent's argmax only where that argmax is unique, otherwise it carries a token outside the
+parent's admissible set.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as U
+from nvfp4_w4a4_block_amd import binding as B
+from nvfp4_w4a4_block_amd import workloads as WL
+from oracle import gemm as G
+from oracle import quant as Q
+from oracle import tree as TR
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    U.require_gpu_lib()
+
+
+def i32(x) -> torch.Tensor:
+    return torch.tensor(np.asarray(x, dtype=np.int32), device="cuda")
+
+
+def tree16():
+    """16 nodes over 8 depths: a main chain with one alternative sibling per depth 1..7 and a
+    last node at depth 8."""
+    parent, chain = [-1], [0]
+    for _ in range(7):
+        parent += [chain[-1], chain[-1]]
+        chain.append(len(parent) - 2)
+    parent.append(chain[-1])
+    return parent
+
+
+def expected_result(parent, draft, greedy):
+    end, path, bonus = TR.accept(parent, draft, greedy)
+    n = len(parent)
+    return end, len(path), bonus, path + [-1] * (n - len(path))
+
+
+def test_tree_accept_matches_oracle_on_random_trees():
+    rng = np.random.default_rng(21)
+    for trial in range(300):
+        n = int(rng.integers(1, 17)) if trial % 10 else 64
+        parent = [-1] + [int(rng.integers(0, v)) for v in range(1, n)]
+        greedy = rng.integers(0, 4, size=n)
+        draft = rng.integers(0, 4, size=n)
+        for v in range(1, n):
+            if rng.random() < 0.6:
+                draft[v] = greedy[parent[v]]
+        res = B.nvfp4_tree_accept(i32(parent), i32(draft), i32(greedy)).cpu().numpy().tolist()
+        end, L, bonus, path = expected_result(parent, draft, greedy)
+        assert res == [end, L, bonus] + path, (trial, parent, draft.tolist(), greedy.tolist())
+
+
+def test_tree_accept_rejects_invalid_parents_without_faulting():
+    # parent indices outside [0, v) reject the node (and its subtree)
+    res = B.nvfp4_tree_accept(i32([-1, 0, 5, -7, 1]), i32([0, 3, 3, 3, 4]), i32([3, 4, 0, 0, 9])).cpu().tolist()
+    assert res == [4, 2, 9, 1, 4, -1, -1, -1]
+
+
+def make_drafts(rng, parent, adm, n_vocab):
+    """Drafts from oracle information only: copy the parent's argmax where it is unique (with
+    probability 0.75), else a token outside the parent's admissible set."""
+    draft = [0]
+    for v in range(1, len(parent)):
+        a = adm[parent[v]]
+        if len(a) == 1 and rng.random() < 0.75:
+            draft.append(next(iter(a)))
+        else:
+            t = (max(a) + 1 + int(rng.integers(0, 1000))) % n_vocab
+            while t in a:
+                t = (t + 1) % n_vocab
+            draft.append(t)
+    return draft
+
+
+def check_verify(ac, asc, ga, wc, wsc, gw, parent, draft, adm, greedy_ref, want_logits, C=None, T=None):
+    greedy, result, logits = B.nvfp4_tree_verify(ac, asc, ga, wc, wsc, gw, i32(parent), i32(draft),
+                                                 want_logits=want_logits)
+    torch.cuda.synchronize()
+    greedy = greedy.cpu().numpy()
+    res = result.cpu().numpy().tolist()
+    for v in range(len(parent)):
+        assert int(greedy[v]) in adm[v], (v, int(greedy[v]), sorted(adm[v])[:8])
+    end, L, bonus, path = expected_result(parent, draft, greedy_ref)
+    assert res[0] == end and res[1] == L and res[3:] == path, (res, end, L, path)
+    assert res[2] in adm[end] and res[2] == int(greedy[end])
+    if want_logits:
+        host = logits.cpu().numpy()
+        assert np.array_equal(np.argmax(host, axis=1), greedy)
+        if C is not None:
+            U.assert_within(host, C, T, "tree_verify logits")
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 256, 1), (3, 1024, 37), (16, 256, 2000), (16, 5120, 3000),
+                                   (16, 1040, 515), (5, 2048, 777)])
+@pytest.mark.parametrize("want_logits", [False, True])
+def test_tree_verify_small(M, K, N, want_logits):
+    if K % 256 and not want_logits:
+        pytest.skip("unfused shapes need the logits buffer (covered with want_logits)")
+    rng = np.random.default_rng(M * 1000 + K + N)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    g_a = Q.global_scale(A)
+    wc, wsc, gw = B.nvfp4_quantize_weights(U.dev_f32(W))
+    ac, asc = B.nvfp4_quantize_act(U.dev_f32(A), U.scalar(g_a))
+    ap, asp = Q.quantize_packed(A, g_a)
+    wp, wsp = Q.quantize_packed(W, Q.global_scale(W))
+    C, T = G.gemm_ref(ap, asp, g_a, wp, wsp, Q.global_scale(W))
+    adm = TR.admissible_argmax(C, T)
+    parent = tree16()[:M] if M <= 16 else None
+    draft = make_drafts(rng, parent, adm, N)
+    check_verify(ac, asc, U.scalar(g_a), wc, wsc, gw, parent, draft, adm, TR.greedy_tokens(C), want_logits, C, T)
+
+
+def _golden_admissible():
+    adm = {}
+    for line in open(os.path.join(GOLDEN, "lm_head_admissible.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        row, cols = line.split(";")
+        adm[int(row)] = {int(c) for c in cols.split()}
+    return [adm[m] for m in range(len(adm))]
+
+
+def _golden_argmax():
+    out = []
+    for line in open(os.path.join(GOLDEN, "lm_head_argmax.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        out.append(int(line.split(";")[1]))
+    return out
+
+
+@pytest.mark.parametrize("want_logits", [False, True])
+def test_tree_verify_lm_head_full_size(want_logits):
+    """The LM head over a 16-node tree at full size (16 x 5120 x 151936), the argmax fused into
+    the GEMM; expected argmax sets from the oracle-written golden files."""
+    wl = WL.get("lm_head")
+    inp = WL.generate(wl)
+    a = inp.a_f32()
+    g_a = Q.global_scale(a)
+    wc, wsc, gw = B.nvfp4_quantize_weights(U.dev_f32(inp.W))
+    ac, asc = B.nvfp4_quantize_act(U.dev_acts(inp), U.scalar(g_a))
+    adm = _golden_admissible()
+    greedy_ref = _golden_argmax()
+    parent = tree16()
+    for seed in range(4):
+        draft = make_drafts(np.random.default_rng(seed), parent, adm, wl.N)
+        check_verify(ac, asc, U.scalar(g_a), wc, wsc, gw, parent, draft, adm, greedy_ref, want_logits)
