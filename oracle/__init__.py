@@ -17,7 +17,9 @@ casts, hand-worked blocks (tests/golden/) and exact rational brute force.
 `tree` adds the greedy verification of a candidate tree over the LM head
 (section "Using tree-based multi-token prediction to accelerate LLM
 inference"), pinned by hand-worked trees and an exhaustive path search.
+`kvfp8` adds the FP8 E4M3 KV-cache codec (same section as NVFP4: the KV cache
+is FP8), pinned by hand-worked elements, exact round trips and torch's casts.
 Parity unpinned by the pages themselves: the per-tensor scale formula
 amax/(6*448) and the static activation scale are readings, not page facts.
 """
-from . import formats, quant, gemm, tree  # noqa: F401
+from . import formats, quant, gemm, tree, kvfp8  # noqa: F401
