@@ -240,12 +240,66 @@ def cpu_baseline(wl: WL.Workload, budget_s: float) -> dict:
                       f"host cpus={len(os.sched_getaffinity(0))}"}
 
 
+def kv_bench(args) -> dict:
+    """FP8 KV-cache codec: one step encodes one layer's bf16 K and V (23,552 tokens x 8 heads x 128)
+    to E4M3 and decodes it back to bf16; 6 bytes of HBM traffic per element (2 + 1, then 1 + 2).
+    Three input/code/output sets rotate so the 256 MB Infinity Cache cannot serve them."""
+    bits = WL.make_kv()
+    n = bits.size
+    x = torch.from_numpy(bits.view(np.int16).reshape(-1)).view(torch.bfloat16).to(DEV)
+    amax = float(torch.max(torch.abs(x.float())))
+    scale = torch.tensor([float(np.float32(np.float32(amax) / np.float32(448.0)))], device=DEV)  # calibration
+    R = 3
+    xs = [x] + [x.clone() for _ in range(R - 1)]
+    qs = [torch.empty(n, dtype=torch.uint8, device=DEV) for _ in range(R)]
+    ys = [torch.empty(n, dtype=torch.bfloat16, device=DEV) for _ in range(R)]
+
+    def step(i):
+        B.nvfp4_kv_fp8_encode(xs[i % R], scale, qs[i % R])
+        B.nvfp4_kv_fp8_decode(qs[i % R], scale, torch.bfloat16, ys[i % R])
+
+    def enc(i):
+        B.nvfp4_kv_fp8_encode(xs[i % R], scale, qs[i % R])
+
+    K, W = args.steps, args.warmup
+    if W:
+        timed_replays(build_graphs(step, R, W), W, R)
+    step_ms = timed_replays(build_graphs(step, R, K), K, R) / K
+    enc_ms = timed_replays(build_graphs(enc, R, K), K, R) / K
+    log(f"[bench] kv_fp8: n={n}, step {step_ms * 1e3:.2f} us, encode {enc_ms * 1e3:.2f} us")
+    roof = {"bound": "hbm", "achieved": 3.0 * n / (enc_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "kernel": "kv_encode_kernel (bf16 -> E4M3)", "traffic": None, "algorithmic_bytes": 3 * n}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    line = {
+        "metric": "FP8 E4M3 KV-cache codec HBM GB/s (bf16 in + E4M3 out, then back)", "value": 6.0 * n / (step_ms * 1e-3) / 1e9,
+        "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": step_ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"kv_fp8: one layer's K and V, {WL.KV_TOKENS} tokens x {WL.KV_HEADS} heads x "
+                               f"{WL.KV_DIM} dims, bf16 <-> E4M3", "elements": n, "copies": R,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import kvfp8 as KVO
+        xs_host = WL.bf16_bits_to_f32(bits.reshape(-1)[: 1 << 22])
+        s = KVO.calibrated_scale(xs_host)
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            KVO.decode_bf16_bits(KVO.encode(xs_host, s), s)
+            reps += 1
+        el = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": 6.0 * xs_host.size * reps / el / 1e9, "unit": "GB/s", "cores": 1,
+                                "kind": "oracle", "sample": f"{reps} x encode + decode of the first {xs_host.size} "
+                                                            f"elements, {el:.1f} s (NumPy, one thread)"}
+    return line
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="decode_up", choices=sorted(WL.WORKLOADS))
+    ap.add_argument("--workload", default="decode_up", choices=sorted(WL.WORKLOADS) + ["kv_fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-reference-mib", type=int, default=0,
@@ -260,6 +314,9 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     B.load()
+    if args.workload == "kv_fp8":
+        print(json.dumps(kv_bench(args)), flush=True)
+        return 0
     wl = WL.get(args.workload)
     P = Pipeline(wl)
     K, W = args.steps, args.warmup

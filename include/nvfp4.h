@@ -157,6 +157,25 @@ nvfp4_status nvfp4_quantize_gemm(int64_t M, int64_t K, int64_t N,
                                  void* out, nvfp4_dtype out_dt, uint8_t* a_codes, uint8_t* a_scales,
                                  void* stream);
 
+/* FP8 E4M3 KV-cache codec: encode.
+ *   x      [n] KV values in x_dt (NVFP4_F32 or NVFP4_BF16), device, any layout
+ *          (the codec is elementwise).
+ *   scale  in: device float, the tensor's static decode scale s (a
+ *          calibration sets s = amax / 448).
+ *   q      out: [n] E4M3FN bytes.
+ * Per element, in correctly rounded fp32: inv = (s == 0) ? 0 : 1 / s,
+ * y = x * inv, q = E4M3(y) rounded to nearest even, saturating at +-448, with
+ * the sign bit of y.  n < 2^40; x and q 16-byte aligned.
+ * Cites: the page section "Using NVFP4 quantization to accelerate
+ * Qwen3.6-27B inference" (the KV cache is FP8). */
+nvfp4_status nvfp4_kv_fp8_encode(const void* x, nvfp4_dtype x_dt, int64_t n, const float* scale, uint8_t* q,
+                                 void* stream);
+
+/* FP8 E4M3 KV-cache codec: decode.  x[i] = fl32(e4m3(q[i]) * s), written as
+ * fp32 or rounded to nearest even bf16 (x_dt).  Arguments as the encoder's. */
+nvfp4_status nvfp4_kv_fp8_decode(const uint8_t* q, int64_t n, const float* scale, void* x, nvfp4_dtype x_dt,
+                                 void* stream);
+
 /* Greedy (temperature-0) acceptance of a verified candidate tree.
  *   n_nodes  1..64 tree nodes in topological order; node 0 is the root.
  *   parent   [n_nodes] int32, device: parent[0] = -1, 0 <= parent[v] < v

@@ -22,7 +22,8 @@ NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_DTYPE, NVF
 NVFP4_F32, NVFP4_BF16 = 0, 1
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 
-EXPORTS = ("nvfp4_abi_version", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_quantize_act",
+EXPORTS = ("nvfp4_abi_version", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_kv_fp8_decode", "nvfp4_kv_fp8_encode",
+           "nvfp4_quantize_act",
            "nvfp4_quantize_gemm", "nvfp4_quantize_weights", "nvfp4_status_string", "nvfp4_tree_accept",
            "nvfp4_tree_verify")
 
@@ -50,9 +51,12 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_gemm_ex.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, i32, p]
     lib.nvfp4_quantize_gemm.argtypes = [i64, i64, i64, p, i32, p, p, p, p, p, i32, p, p, p]
     lib.nvfp4_tree_accept.argtypes = [i64, p, p, p, p, p]
+    lib.nvfp4_kv_fp8_encode.argtypes = [p, i32, i64, p, p, p]
+    lib.nvfp4_kv_fp8_decode.argtypes = [p, i64, p, p, i32, p]
     lib.nvfp4_tree_verify.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p, p, p, p, p, p]
     for f in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "nvfp4_gemm", "nvfp4_gemm_ex",
-              "nvfp4_quantize_gemm", "nvfp4_tree_accept", "nvfp4_tree_verify"):
+              "nvfp4_quantize_gemm", "nvfp4_tree_accept", "nvfp4_tree_verify", "nvfp4_kv_fp8_encode",
+              "nvfp4_kv_fp8_decode"):
         getattr(lib, f).restype = i32
     lib.nvfp4_status_string.argtypes = [i32]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
@@ -260,3 +264,37 @@ def nvfp4_tree_verify(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: torch.
                                     greedy.data_ptr(), result.data_ptr(), keys.data_ptr(), _stream(dev)),
            "nvfp4_tree_verify")
     return greedy, result, logits
+
+
+def nvfp4_kv_fp8_encode(x: torch.Tensor, scale: torch.Tensor, q: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """KV values x (float32/bfloat16, any shape, contiguous) with device decode scale [1] -> E4M3
+    bytes (uint8, same shape)."""
+    if scale.dtype != torch.float32 or scale.numel() != 1:
+        raise ValueError("scale must be a float32 tensor of one element")
+    dev = _dev(x, scale)
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+    elif q.dtype != torch.uint8 or q.numel() != x.numel():
+        raise ValueError("q must be uint8 with x's element count")
+    _dev(x, q)
+    _check(load().nvfp4_kv_fp8_encode(x.data_ptr(), _dt(x.dtype), x.numel(), scale.data_ptr(), q.data_ptr(),
+                                      _stream(dev)), "nvfp4_kv_fp8_encode")
+    return q
+
+
+def nvfp4_kv_fp8_decode(q: torch.Tensor, scale: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """E4M3 bytes q (uint8) with device decode scale [1] -> values (out_dtype, same shape)."""
+    if q.dtype != torch.uint8:
+        raise ValueError("q must be uint8")
+    if scale.dtype != torch.float32 or scale.numel() != 1:
+        raise ValueError("scale must be a float32 tensor of one element")
+    dev = _dev(q, scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=dev)
+    elif out.dtype != out_dtype or out.numel() != q.numel():
+        raise ValueError("out must have q's element count and out_dtype")
+    _dev(q, out)
+    _check(load().nvfp4_kv_fp8_decode(q.data_ptr(), q.numel(), scale.data_ptr(), out.data_ptr(), _dt(out_dtype),
+                                      _stream(dev)), "nvfp4_kv_fp8_decode")
+    return out

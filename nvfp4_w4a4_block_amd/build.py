@@ -29,6 +29,7 @@ SOURCES = {
     "gemv_fp4.hip": [],
     "gemm_m16.hip": [],
     "tree.hip": [],
+    "kv_fp8.hip": [],
     "gemm_tiled.hip": [],
     "abi.cpp": [],
 }

@@ -41,7 +41,7 @@ const char* nvfp4_status_string(nvfp4_status s) {
   return "unknown status";
 }
 
-int nvfp4_abi_version(void) { return 3; }
+int nvfp4_abi_version(void) { return 4; }
 
 nvfp4_status nvfp4_quantize_weights(const void* w, nvfp4_dtype w_dt, int64_t N, int64_t K,
                                     uint8_t* w_codes, uint8_t* w_scales, float* w_global,
@@ -148,6 +148,26 @@ nvfp4_status nvfp4_quantize_gemm(int64_t M, int64_t K, int64_t N,
   hipError_t e = nvfp4::launch_quantize(a, a_dt == NVFP4_BF16, M, K, a_global, a_codes, a_scales, s);
   if (e != hipSuccess || N == 0) return from_hip(e);
   return from_hip(M <= 16 ? nvfp4::launch_gemm_skinny(g, s) : nvfp4::launch_gemm_tiled(g, s));
+}
+
+nvfp4_status nvfp4_kv_fp8_encode(const void* x, nvfp4_dtype x_dt, int64_t n, const float* scale, uint8_t* q,
+                                 void* stream) {
+  if (!dtype_ok(x_dt)) return NVFP4_ERR_DTYPE;
+  if (n < 0 || n >= ((int64_t)1 << 40)) return NVFP4_ERR_SHAPE;
+  if (n == 0) return NVFP4_OK;
+  if (!x || !scale || !q) return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned4(scale)) return NVFP4_ERR_ALIGN;
+  return from_hip(nvfp4::launch_kv_fp8_encode(x, x_dt == NVFP4_BF16, n, scale, q, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_kv_fp8_decode(const uint8_t* q, int64_t n, const float* scale, void* x, nvfp4_dtype x_dt,
+                                 void* stream) {
+  if (!dtype_ok(x_dt)) return NVFP4_ERR_DTYPE;
+  if (n < 0 || n >= ((int64_t)1 << 40)) return NVFP4_ERR_SHAPE;
+  if (n == 0) return NVFP4_OK;
+  if (!x || !scale || !q) return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned4(scale)) return NVFP4_ERR_ALIGN;
+  return from_hip(nvfp4::launch_kv_fp8_decode(q, n, scale, x, x_dt == NVFP4_BF16, static_cast<hipStream_t>(stream)));
 }
 
 nvfp4_status nvfp4_tree_accept(int64_t n_nodes, const int32_t* parent, const int32_t* draft, const int32_t* greedy,

@@ -42,6 +42,12 @@ struct GemmArgs {
 
 constexpr int kKeySlots = 64;  // argmax key slots per row
 
+// FP8 E4M3 KV-cache codec (kv_fp8.hip).
+hipError_t launch_kv_fp8_encode(const void* x, bool bf16, int64_t n, const float* scale, uint8_t* q,
+                                hipStream_t stream);
+hipError_t launch_kv_fp8_decode(const uint8_t* q, int64_t n, const float* scale, void* x, bool bf16,
+                                hipStream_t stream);
+
 // Greedy tree verification over the LM head (tree.hip).  The argmax keys
 // ([kKeySlots][16]) are reduced, and reset to zero, by the acceptance kernel.
 hipError_t launch_argmax_rows(const float* logits, int M, int N, uint64_t* keys, hipStream_t stream);

@@ -146,3 +146,23 @@ def generate(wl: Workload, *, M: Optional[int] = None, K: Optional[int] = None,
     A = make_acts(rng, M, K, wl.act, wl.act_dtype, outlier_frac=wl.outlier_frac,
                   outlier_gain=wl.outlier_gain, zero_frac=wl.zero_frac)
     return Inputs(wl, W, A, W2)
+
+
+# KV cache of one attention layer for the FP8 codec: K and V of a context as long as the
+# benchmark's longest agent turns (about 23.5K prompt tokens on the page "TensorRT Edge-LLM
+# Completes the MLPerf Edge Agentic Benchmark 6.4x Faster on Jetson AGX Thor"), 8 KV heads of
+# dimension 128 (grouped-query attention of a model of this size; the pages give no layer
+# shapes).  Values N(0, 1) with 1% of the channels of each head scaled by 8 (keys carry a few
+# large channels); stored as bf16.
+KV_TOKENS, KV_HEADS, KV_DIM = 23552, 8, 128
+
+
+def make_kv(seed: int = 0, tokens: int = KV_TOKENS, heads: int = KV_HEADS, dim: int = KV_DIM) -> np.ndarray:
+    """uint16 bf16 bit patterns of [2, tokens, heads, dim] (K then V)."""
+    rng = np.random.default_rng(seed)
+    kv = rng.standard_normal((2, tokens, heads, dim), dtype=np.float32)
+    n_out = max(1, int(round(0.01 * dim)))
+    for h in range(heads):
+        cols = rng.choice(dim, size=n_out, replace=False)
+        kv[0, :, h, cols] *= np.float32(8.0)
+    return f32_to_bf16_bits(kv)

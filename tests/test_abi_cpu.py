@@ -42,7 +42,7 @@ def test_status_strings_and_version(lib):
     for s in range(6):
         assert B.status_string(s)
     assert B.status_string(99) == "unknown status"
-    assert lib.nvfp4_abi_version() == 3
+    assert lib.nvfp4_abi_version() == 4
 
 
 def gemm(lib, M, K, N, ptrs=(A16,) * 7, out_dt=B.NVFP4_BF16, path=B.PATH_AUTO):
@@ -148,3 +148,15 @@ def test_tree_entry_points_validate(lib):
     assert verify(16, 5120, 100, tuple(ptrs)) == B.NVFP4_ERR_NULL
     # logits may be omitted only where the argmax is fused (K % 256 == 0, K <= 5120)
     assert verify(16, 1040, 100, logits=None) == B.NVFP4_ERR_NULL
+
+
+def test_kv_fp8_validation(lib):
+    A = A16
+    for f in (lambda *a: lib.nvfp4_kv_fp8_encode(a[0], a[4], a[1], a[2], a[3], None),
+              lambda *a: lib.nvfp4_kv_fp8_decode(a[3], a[1], a[2], a[0], a[4], None)):
+        assert f(A, 100, A, A, 9) == B.NVFP4_ERR_DTYPE
+        assert f(A, -1, A, A, B.NVFP4_BF16) == B.NVFP4_ERR_SHAPE
+        assert f(None, 0, None, None, B.NVFP4_BF16) == B.NVFP4_OK
+        assert f(None, 100, A, A, B.NVFP4_BF16) == B.NVFP4_ERR_NULL
+        assert f(A, 100, A + 2, A, B.NVFP4_BF16) == B.NVFP4_ERR_ALIGN
+        assert f(A + 8, 100, A, A, B.NVFP4_BF16) == B.NVFP4_ERR_ALIGN
