@@ -22,6 +22,22 @@ __device__ __forceinline__ uint32_t encode_e4m3_signed(float y) {
   return e4m3_from_nonneg(__builtin_fabsf(y)) | ((__float_as_uint(y) >> 24) & 0x80u);
 }
 
+// Four values -> four E4M3 bytes (value i in byte i) with the hardware
+// conversion after clamping to +-448.  On gfx950 this equals
+// encode_e4m3_signed for every finite input (checked on 50M inputs: every
+// E4M3 midpoint and its float32 neighbours, subnormals, signed zeros and
+// saturating values): round to nearest even, and the clamp supplies the
+// saturation that the conversion alone would turn into NaN.
+__device__ __forceinline__ uint32_t encode4_e4m3(float a, float b, float c, float d) {
+  const float lo = -448.0f, hi = 448.0f;
+  a = __builtin_fminf(__builtin_fmaxf(a, lo), hi);
+  b = __builtin_fminf(__builtin_fmaxf(b, lo), hi);
+  c = __builtin_fminf(__builtin_fmaxf(c, lo), hi);
+  d = __builtin_fminf(__builtin_fmaxf(d, lo), hi);
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
 template <bool BF16>
 __device__ __forceinline__ void load16(const void* x, int64_t c, float* v) {
   if constexpr (BF16) {
@@ -65,9 +81,10 @@ __global__ __launch_bounds__(256) void kv_encode_kernel(const void* x, int64_t n
 #pragma unroll
     for (int u = 0; u < kChunksPerThread; ++u) {
       if (c0 + u * T < chunks) {
-        u4_t w = {0u, 0u, 0u, 0u};
+        u4_t w;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) w[i >> 2] |= encode_e4m3_signed(v[u][i] * inv) << (8 * (i & 3));
+        for (int j = 0; j < 4; ++j)
+          w[j] = encode4_e4m3(v[u][4 * j] * inv, v[u][4 * j + 1] * inv, v[u][4 * j + 2] * inv, v[u][4 * j + 3] * inv);
         reinterpret_cast<u4_t*>(q)[c0 + u * T] = w;
       }
     }
