@@ -112,8 +112,12 @@ class Pipeline:
             amax = self.y1.float().abs().max().item()
             self.g2 = torch.tensor([float(np.float32(np.float32(amax) / np.float32(2688.0)))], device=DEV)
 
+    dynamic_scale = False  # set by --dynamic-act-scale: g_a computed on the device every step
+
     def _gemm1(self, i):
         wc, ws, gw = self.l1.copies[i % self.R]
+        if self.dynamic_scale:
+            B.nvfp4_act_global_scale(self.a, out=self.g1)
         B.nvfp4_quantize_gemm(self.a, self.g1, wc, ws, gw, out_dtype=self.out_dtype, out=self.y1,
                               a_codes=self.ac1, a_scales=self.as1)
 
@@ -131,6 +135,8 @@ class Pipeline:
         self._gemm1(i)
         if self.l2 is not None:
             wc, ws, gw = self.l2.copies[i % self.R]
+            if self.dynamic_scale:
+                B.nvfp4_act_global_scale(self.y1, out=self.g2)
             B.nvfp4_quantize_gemm(self.y1, self.g2, wc, ws, gw, out_dtype=self.out_dtype, out=self.y2,
                                   a_codes=self.ac2, a_scales=self.as2)
 
@@ -301,6 +307,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode_up", choices=sorted(WL.WORKLOADS) + ["kv_fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dynamic-act-scale", action="store_true",
+                    help="compute the activation scale on the device in every step (nvfp4_act_global_scale) "
+                         "instead of the static calibrated one")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-reference-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (a known-size "
@@ -318,6 +327,7 @@ def main() -> int:
         print(json.dumps(kv_bench(args)), flush=True)
         return 0
     wl = WL.get(args.workload)
+    Pipeline.dynamic_scale = args.dynamic_act_scale
     P = Pipeline(wl)
     K, W = args.steps, args.warmup
 
@@ -353,7 +363,8 @@ def main() -> int:
         "dtype": "f16", "data": "synthetic",
         "config": {"workload": f"{wl.name}: M={wl.M} K={wl.K} N={wl.N} ({wl.note})", "M": wl.M, "K": wl.K,
                    "N": wl.N, "act_dtype": wl.act_dtype, "out_dtype": wl.out_dtype,
-                   "weight_copies": P.R, "parallelism": "none (1 GPU)"},
+                   "weight_copies": P.R, "parallelism": "none (1 GPU)",
+                   "act_scale": "dynamic (device amax per step)" if args.dynamic_act_scale else "static (calibrated)"},
         "roofline": roof,
     }
     if args.copy_reference_mib:

@@ -110,6 +110,21 @@ nvfp4_status nvfp4_quantize_act(const void* a, nvfp4_dtype a_dt, int64_t M, int6
                                 const float* a_global, uint8_t* a_codes, uint8_t* a_scales,
                                 void* stream);
 
+/* Dynamic activation tensor scale, computed on the device from the
+ * activations themselves instead of a static calibrated value.
+ *   a         [M][K] in a_dt (NVFP4_F32 or NVFP4_BF16), device.
+ *   a_global  out: one float, g_a = fl32(amax|A| / 2688) (0 for an all-zero
+ *             A): the weights' formula.  Also the amax accumulator for large
+ *             tensors, so it must not alias any other argument.
+ * Stream-ordered before nvfp4_quantize_act / nvfp4_quantize_gemm, which read
+ * it from the device.  One kernel up to 2^20 elements (a decode row), three
+ * beyond.
+ * Cites: the page section "Using NVFP4 quantization to accelerate Qwen3.6-27B
+ * inference" (activations are NVFP4; the pages stress a calibrated checkpoint,
+ * of which this is the dynamic alternative). */
+nvfp4_status nvfp4_act_global_scale(const void* a, nvfp4_dtype a_dt, int64_t M, int64_t K, float* a_global,
+                                    void* stream);
+
 /* NVFP4 W4A4 GEMM:  out[m][n] = g_a * g_w * sum_k e2m1(qa)*sa * e2m1(qw)*sw.
  *   a_codes [M][K/2], a_scales [M][K/16], a_global (device float): activations.
  *   w_codes [N][K/2], w_scales [N][K/16], w_global (device float): weights.

@@ -22,7 +22,7 @@ NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_DTYPE, NVF
 NVFP4_F32, NVFP4_BF16 = 0, 1
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 
-EXPORTS = ("nvfp4_abi_version", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_kv_fp8_decode", "nvfp4_kv_fp8_encode",
+EXPORTS = ("nvfp4_abi_version", "nvfp4_act_global_scale", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_kv_fp8_decode", "nvfp4_kv_fp8_encode",
            "nvfp4_quantize_act",
            "nvfp4_quantize_gemm", "nvfp4_quantize_weights", "nvfp4_status_string", "nvfp4_tree_accept",
            "nvfp4_tree_verify")
@@ -52,11 +52,12 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_quantize_gemm.argtypes = [i64, i64, i64, p, i32, p, p, p, p, p, i32, p, p, p]
     lib.nvfp4_tree_accept.argtypes = [i64, p, p, p, p, p]
     lib.nvfp4_kv_fp8_encode.argtypes = [p, i32, i64, p, p, p]
+    lib.nvfp4_act_global_scale.argtypes = [p, i32, i64, i64, p, p]
     lib.nvfp4_kv_fp8_decode.argtypes = [p, i64, p, p, i32, p]
     lib.nvfp4_tree_verify.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p, p, p, p, p, p]
     for f in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "nvfp4_gemm", "nvfp4_gemm_ex",
               "nvfp4_quantize_gemm", "nvfp4_tree_accept", "nvfp4_tree_verify", "nvfp4_kv_fp8_encode",
-              "nvfp4_kv_fp8_decode"):
+              "nvfp4_kv_fp8_decode", "nvfp4_act_global_scale"):
         getattr(lib, f).restype = i32
     lib.nvfp4_status_string.argtypes = [i32]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
@@ -297,4 +298,20 @@ def nvfp4_kv_fp8_decode(q: torch.Tensor, scale: torch.Tensor, out_dtype: torch.d
     _dev(q, out)
     _check(load().nvfp4_kv_fp8_decode(q.data_ptr(), q.numel(), scale.data_ptr(), out.data_ptr(), _dt(out_dtype),
                                       _stream(dev)), "nvfp4_kv_fp8_decode")
+    return out
+
+
+def nvfp4_act_global_scale(a: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dynamic activation decode scale g_a = amax|a| / 2688 of a [M, K] float32/bfloat16 tensor,
+    computed on the device -> float32 [1] (device)."""
+    if a.dim() != 2:
+        raise ValueError("a must be [M, K]")
+    dev = _dev(a)
+    if out is None:
+        out = torch.empty((1,), dtype=torch.float32, device=dev)
+    elif out.dtype != torch.float32 or out.numel() != 1:
+        raise ValueError("out must be a float32 tensor of one element")
+    M, K = a.shape
+    _check(load().nvfp4_act_global_scale(a.data_ptr(), _dt(a.dtype), M, K, out.data_ptr(), _stream(dev)),
+           "nvfp4_act_global_scale")
     return out

@@ -41,7 +41,7 @@ const char* nvfp4_status_string(nvfp4_status s) {
   return "unknown status";
 }
 
-int nvfp4_abi_version(void) { return 4; }
+int nvfp4_abi_version(void) { return 5; }
 
 nvfp4_status nvfp4_quantize_weights(const void* w, nvfp4_dtype w_dt, int64_t N, int64_t K,
                                     uint8_t* w_codes, uint8_t* w_scales, float* w_global,
@@ -59,6 +59,19 @@ nvfp4_status nvfp4_quantize_weights(const void* w, nvfp4_dtype w_dt, int64_t N, 
   hipError_t e = nvfp4::launch_weight_global(w, bf16, N * K, w_global, s);
   if (e != hipSuccess || N == 0) return from_hip(e);
   return from_hip(nvfp4::launch_quantize(w, bf16, N, K, w_global, w_codes, w_scales, s));
+}
+
+nvfp4_status nvfp4_act_global_scale(const void* a, nvfp4_dtype a_dt, int64_t M, int64_t K, float* a_global,
+                                    void* stream) {
+  if (!dtype_ok(a_dt)) return NVFP4_ERR_DTYPE;
+  if (!shape_ok(M, K)) return NVFP4_ERR_SHAPE;
+  if (!a_global) return NVFP4_ERR_NULL;
+  if (!aligned4(a_global)) return NVFP4_ERR_ALIGN;
+  if (M > 0) {
+    if (!a) return NVFP4_ERR_NULL;
+    if (!aligned16(a)) return NVFP4_ERR_ALIGN;
+  }
+  return from_hip(nvfp4::launch_act_global(a, a_dt == NVFP4_BF16, M * K, a_global, static_cast<hipStream_t>(stream)));
 }
 
 nvfp4_status nvfp4_quantize_act(const void* a, nvfp4_dtype a_dt, int64_t M, int64_t K,

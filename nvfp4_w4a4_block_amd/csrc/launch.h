@@ -15,6 +15,8 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t K, co
 // g = amax|w| / 2688 over `elems` elements, written to the device float `g`.
 hipError_t launch_weight_global(const void* w, bool bf16, int64_t elems, float* g,
                                 hipStream_t stream);
+// The same for activations; one workgroup and one launch up to 2^20 elements.
+hipError_t launch_act_global(const void* a, bool bf16, int64_t elems, float* g, hipStream_t stream);
 
 struct GemmArgs {
   int M, K, N;

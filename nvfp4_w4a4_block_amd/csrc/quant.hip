@@ -107,6 +107,34 @@ __global__ void finalize_global_kernel(uint32_t* p) {
   *reinterpret_cast<float*>(p) = amax / 2688.0f;
 }
 
+// One workgroup computes g = fl32(amax / 2688) of a small tensor directly (no
+// atomics, no clearing launch): the decode step's single activation row.
+constexpr int kSmallAmaxThreads = 1024;
+constexpr int64_t kSmallAmaxMax = (int64_t)1 << 20;  // elements served by one workgroup
+
+template <typename In>
+__global__ __launch_bounds__(kSmallAmaxThreads) void amax_small_kernel(const In* __restrict__ x, int64_t n8,
+                                                                       float* __restrict__ g) {
+  float m = 0.0f;
+  for (int64_t t = threadIdx.x; t < n8; t += kSmallAmaxThreads) {
+    float v[8];
+    load8(x + t * 8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+  __shared__ float wave_max[kSmallAmaxThreads / 64];
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = wave_max[0];
+#pragma unroll
+    for (int i = 1; i < kSmallAmaxThreads / 64; ++i) b = __builtin_fmaxf(b, wave_max[i]);
+    *g = b / 2688.0f;
+  }
+}
+
 template <typename In>
 hipError_t launch_quant_blocks(const void* x, int64_t elems, const float* g, uint8_t* codes,
                                uint8_t* scales, hipStream_t stream) {
@@ -139,6 +167,13 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t K, co
   const int64_t elems = rows * K;
   return bf16 ? launch_quant_blocks<uint16_t>(x, elems, g, codes, scales, stream)
               : launch_quant_blocks<float>(x, elems, g, codes, scales, stream);
+}
+
+hipError_t launch_act_global(const void* a, bool bf16, int64_t elems, float* g, hipStream_t stream) {
+  if (elems > kSmallAmaxMax) return launch_weight_global(a, bf16, elems, g, stream);
+  if (bf16) amax_small_kernel<uint16_t><<<1, kSmallAmaxThreads, 0, stream>>>(static_cast<const uint16_t*>(a), elems / 8, g);
+  else amax_small_kernel<float><<<1, kSmallAmaxThreads, 0, stream>>>(static_cast<const float*>(a), elems / 8, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_weight_global(const void* w, bool bf16, int64_t elems, float* g,

@@ -42,7 +42,7 @@ def test_status_strings_and_version(lib):
     for s in range(6):
         assert B.status_string(s)
     assert B.status_string(99) == "unknown status"
-    assert lib.nvfp4_abi_version() == 4
+    assert lib.nvfp4_abi_version() == 5
 
 
 def gemm(lib, M, K, N, ptrs=(A16,) * 7, out_dt=B.NVFP4_BF16, path=B.PATH_AUTO):
@@ -160,3 +160,13 @@ def test_kv_fp8_validation(lib):
         assert f(None, 100, A, A, B.NVFP4_BF16) == B.NVFP4_ERR_NULL
         assert f(A, 100, A + 2, A, B.NVFP4_BF16) == B.NVFP4_ERR_ALIGN
         assert f(A + 8, 100, A, A, B.NVFP4_BF16) == B.NVFP4_ERR_ALIGN
+
+
+def test_act_global_scale_validation(lib):
+    A = A16
+    assert lib.nvfp4_act_global_scale(A, 9, 1, 16, A, None) == B.NVFP4_ERR_DTYPE
+    assert lib.nvfp4_act_global_scale(A, B.NVFP4_BF16, 1, 24, A, None) == B.NVFP4_ERR_SHAPE
+    assert lib.nvfp4_act_global_scale(A, B.NVFP4_BF16, 1, 16, None, None) == B.NVFP4_ERR_NULL
+    assert lib.nvfp4_act_global_scale(None, B.NVFP4_BF16, 1, 16, A, None) == B.NVFP4_ERR_NULL
+    assert lib.nvfp4_act_global_scale(A, B.NVFP4_BF16, 1, 16, A + 2, None) == B.NVFP4_ERR_ALIGN
+    assert lib.nvfp4_act_global_scale(A + 8, B.NVFP4_BF16, 1, 16, A, None) == B.NVFP4_ERR_ALIGN
