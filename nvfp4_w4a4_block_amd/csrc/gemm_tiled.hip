@@ -154,205 +154,341 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(GemmArgs p) {
 
 
 // ---------------------------------------------------------------------------
-// Wave-tiled path for K % 128 == 0 (prefill shapes).  Every wave owns a
-// 128 x 80 output tile (8 x 5 MFMA tiles of 16 x 16, 160 accumulators per
-// lane) over a quarter of K; the four waves of a workgroup hold the same tile
-// and split K, and their partial sums are added in a fixed order through LDS
-// at the end.  A 128 x 80 tile makes both prefill GEMMs (512 x 25600 and
-// 512 x 5120 outputs) exact multiples of 256 workgroups, one per CU per round.
+// Persistent workgroup-tiled path for K % 1024 == 0 (prefill shapes).
 //
-// Operands come from global memory (mostly L2) in the MFMA lane layout: lane
-// l = r + 16*q of a 16-row tile takes 16 bytes (32 codes) of row r at K
-// offset 32*q of a 128-K step and the 2 scale bytes of those two blocks; each
-// 8-code slice feeds one 16x16x32 f16 MFMA (the same K permutation on both
-// operands, so the sum is unchanged).  Dequantization is per wave: 208 rows
-// converted per K-step for 10240 outputs.
+// Output tile 64 x 160 per workgroup (2 x 5 MFMA tiles of 32 x 32, f16
+// 32x32x16 matrix instructions).  Both prefill GEMMs (512 x 25600 and
+// 512 x 5120 outputs) are exact multiples of 256 such tiles.  One workgroup per
+// CU walks its tiles in turn, and the load pipeline runs on across tile
+// boundaries.  Eight waves (two per SIMD: while one waits on its matrix
+// instruction the other issues its dequantization) each hold the whole tile
+// (160 accumulators per lane) over an eighth of every 256-K step and add their
+// partial sums in a fixed order through LDS when the tile is done.  A wave
+// dequantizes only its own eighth, so every operand element is converted to
+// f16 exactly once per workgroup.
 //
-// Latency hiding with one wave per SIMD: the codes of the next two K-steps
-// stream into a private 3-slot LDS ring through buffer->LDS loads (no
-// registers held in flight); at the start of a step the wave reads its codes
-// back (each lane its own 16 bytes per tile, conflict-free) and the scale
-// bytes, loaded into a small register ring, are already there.  Rows past M
-// or N lie past the end of their buffers and read as zeros.
+// Loads: the workgroup stages each 256-K step (14 tiles of 16 rows x 128 code
+// bytes: 4 of A, 10 of B) in a 3-slot LDS ring with buffer->LDS loads, each
+// instruction 8 rows x 128 bytes, so that every four consecutive lanes read 64
+// contiguous bytes: the L1 cache then takes 16 accesses per instruction, not
+// one per lane.  Scale bytes (16 per row and step) come 4 steps at a time into
+// a 2-slot LDS buffer, 16 rows x 64 bytes per instruction.  The 16-byte chunks
+// of a row are XOR-swizzled by the row index inside LDS, so the MFMA-layout
+// reads spread over the banks.  Rows past M or N lie past the end of their
+// buffers and read as zeros.
 //
-// Workgroup order: consecutive workgroups go to different XCDs; the tile
-// index is remapped so that each XCD walks a contiguous range of tiles with
-// the M-tiles innermost, and the four M-tiles that share a weight tile run on
-// the same XCD and meet it in that XCD's L2.
+// Schedule of step g: wait for this wave's loads of step g + 1, barrier (no
+// memory fence), read step g + 1's codes and scale bytes from LDS into the
+// other register set, issue the loads of step g + 3 into the slot step g used
+// (every wave is past its reads) and, at a group start, the next scale group;
+// then multiply step g.  LDS latency hides behind the multiplies.
 // ---------------------------------------------------------------------------
-constexpr int WTM = 8, WTN = 5, WKS = 4;       // 16-row A tiles, 16-row B tiles, K split
-constexpr int WT = WTM + WTN;                   // 16-row tiles per wave
-constexpr int kSlots = 3;                       // LDS ring depth (K-steps)
-constexpr int kSlotBytes = WT * 1024;           // codes of one K-step: 64 lanes x 16 bytes per tile
-constexpr int kWaveLds = kSlots * kSlotBytes;
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int MT = 2, NT = 5;                // 32 x 32 MFMA tiles per workgroup tile
+constexpr int FT = MT + NT;                  // MFMA operand tiles
+constexpr int BMW = 32 * MT, BNW = 32 * NT;  // 64 x 160 outputs
+constexpr int TA = BMW / 16, TT = TA + BNW / 16;  // 16-row load tiles: 4 of A, 14 in all
+constexpr int kWaves = 8;
+constexpr int kStepK = 256;                  // 128 code bytes per row per step
+constexpr int kTileStep = 16 * 128;          // one 16-row tile of one step
+constexpr int kSlotBytes = TT * kTileStep;   // 28 KiB
+constexpr int kSlots = 3;
+constexpr int kGroup = 4;                    // steps per scale group
+constexpr int kScaleTile = 16 * 64;          // 16 rows x 64 scale bytes
+constexpr int kScaleBuf = TT * kScaleTile;   // 14 KiB
+constexpr int kRedBytes = kWaves * 64 * 64;  // one accumulator tile of every wave
+constexpr int kScaleOff = kSlots * kSlotBytes;
+constexpr int kRedOff = kScaleOff + 2 * kScaleBuf;
+constexpr int kLdsBytes = kRedOff + kRedBytes;  // 144 KiB
+constexpr int kCodeLoadsMax = 4;             // per wave and step: 4 (waves 0-3) or 3 (waves 4-7)
+constexpr int kScaleLoads = 2;               // per wave and group
+static_assert(kWaves * 3 + 4 == 2 * TT, "every half of every load tile is issued once per step");
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-// s_waitcnt immediate for "at most n vector-memory operations outstanding".
+// s_waitcnt immediates: "at most n vector-memory operations outstanding", and
+// "all LDS operations done".
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define W_(k) case k: __builtin_amdgcn_s_waitcnt(vmcnt_imm(k)); break;
+    W_(1) W_(2) W_(3) W_(4) W_(5) W_(6) W_(7) W_(8) W_(9) W_(10) W_(11) W_(12)
+#undef W_
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;  // also safe for any other count
+  }
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are done,
+// no wait on vector memory (loads of later steps stay in flight), and the
+// compiler moves no memory access across it.
+__device__ __forceinline__ void barrier_lds() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kLgkm0);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ f32x16_t mfma32x32x16(h8_t a, h8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 template <bool OUT_BF16>
-__global__ __launch_bounds__(64 * WKS) void gemm_wave_tiled_kernel(GemmArgs p, int tiles_m, int tiles_n) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t wt_lds[];
+__global__ __launch_bounds__(64 * kWaves) void gemm_wg_tiled_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 15, q = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r32 = lane & 31, kq = lane >> 5;
   const int M = p.M, K = p.K, N = p.N;
-
   const int total = tiles_m * tiles_n;
-  const int bid = blockIdx.x;
-  const int L = (total % 8 == 0) ? (bid % 8) * (total / 8) + bid / 8 : bid;
-  const int tm = L % tiles_m, tn = L / tiles_m;
-  const int m0 = tm * 16 * WTM, n0 = tn * 16 * WTN;
+  const int grid = gridDim.x, b = blockIdx.x;
+  const int my_tiles = (total - b + grid - 1) / grid;
+  const int steps = K / kStepK;  // a multiple of kGroup
+  const int groups = steps / kGroup;
+  const int total_steps = my_tiles * steps;
 
   const uint32_t cstride = (uint32_t)K >> 1, sstride = (uint32_t)K >> 4;
-  const __amdgpu_buffer_rsrc_t ac = __builtin_amdgcn_make_buffer_rsrc(
+  const __amdgpu_buffer_rsrc_t rac = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.ac), (short)0, (int)((uint32_t)M * cstride), 0x00020000);
-  const __amdgpu_buffer_rsrc_t as = __builtin_amdgcn_make_buffer_rsrc(
+  const __amdgpu_buffer_rsrc_t ras = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.as), (short)0, (int)((uint32_t)M * sstride), 0x00020000);
-  const __amdgpu_buffer_rsrc_t wc = __builtin_amdgcn_make_buffer_rsrc(
+  const __amdgpu_buffer_rsrc_t rwc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.wc), (short)0, (int)((uint32_t)N * cstride), 0x00020000);
-  const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
+  const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.ws), (short)0, (int)((uint32_t)N * sstride), 0x00020000);
 
-  constexpr uint32_t OOB = 0x80000000u;
-  const uint32_t a_c0 = (uint32_t)(m0 + r) * cstride + 16 * q, a_s0 = (uint32_t)(m0 + r) * sstride + 2 * q;
-  const uint32_t b_c0 = (uint32_t)(n0 + r) * cstride + 16 * q, b_s0 = (uint32_t)(n0 + r) * sstride + 2 * q;
-  const uint32_t tc = 16 * cstride, ts = 16 * sstride;  // bytes between consecutive 16-row tiles
-
-  const int steps = K >> 7;
-  const int s_begin = (steps * wave) / WKS, s_end = (steps * (wave + 1)) / WKS;
-  const int my = s_end - s_begin;
-
-  uint8_t* ring = wt_lds + wave * kWaveLds;
-
-  // Codes of step i -> LDS slot (i % kSlots): WT buffer->LDS loads.
-  auto dma_step = [&](int i) {
-    const bool ok = i < my;
-    const uint32_t co = (uint32_t)(s_begin + i) * 64;
-    uint8_t* slot = ring + (i % kSlots) * kSlotBytes;
-#pragma unroll
-    for (int t = 0; t < WTM; ++t)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ac, LDS_PTR(slot + t * 1024), 16,
-                                               ok ? a_c0 + t * tc + co : OOB, 0, 0, 0);
-#pragma unroll
-    for (int t = 0; t < WTN; ++t)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wc, LDS_PTR(slot + (WTM + t) * 1024), 16,
-                                               ok ? b_c0 + t * tc + co : OOB, 0, 0, 0);
-  };
-  // Scale bytes of step i: one 16-bit load per tile (2 blocks of the lane's run).
-  struct Scales { uint32_t v[WT]; };
-  auto load_scales = [&](int i) {
-    Scales sc;
-    const bool ok = i < my;
-    const uint32_t so = (uint32_t)(s_begin + i) * 8;
-#pragma unroll
-    for (int t = 0; t < WTM; ++t)
-      sc.v[t] = __builtin_amdgcn_raw_buffer_load_b16(as, ok ? a_s0 + t * ts + so : OOB, 0, 0);
-#pragma unroll
-    for (int t = 0; t < WTN; ++t)
-      sc.v[WTM + t] = __builtin_amdgcn_raw_buffer_load_b16(ws, ok ? b_s0 + t * ts + so : OOB, 0, 0);
-    return sc;
+  // Tile it of this workgroup -> first output row and column.  Consecutive
+  // workgroups run on different XCDs; with total % 8 == 0 each XCD walks a
+  // contiguous range of tiles, M-tiles innermost, so the M-tiles that share a
+  // weight tile meet it in one L2.
+  auto coords = [&](int it, int& mb, int& nb) {
+    const int idx = it * grid + b;
+    const int L = (total % 8 == 0) ? (idx % 8) * (total / 8) + idx / 8 : idx;
+    mb = (L % tiles_m) * BMW;
+    nb = (L / tiles_m) * BNW;
   };
 
-  f4_t acc[WTM][WTN];
+  // This wave's loads.  Codes: load k (k < 4 for waves 0-3, k < 3 for waves
+  // 4-7) takes rows 8h..8h+7 (h = w & 1) of load tile (w >> 1) + 4k (tiles 0-3
+  // are A rows, 4-13 B rows).  Lane l reads row 8h + l/8, 16-byte chunk
+  // (l % 8) ^ (l / 8) of the step and lands at LDS byte 16 l of the
+  // instruction: chunk c of row j sits at 16 * (8 j + (c ^ (j & 7))) inside its
+  // tile.  Scales: load k = 0, 1 takes load tile min(w + 8k, 13) (waves 6-7
+  // repeat wave 5's second load: the same bytes to the same place); lane l
+  // reads row l/4, chunk (l % 4) ^ ((l / 8) & 3) of the group's 64 bytes, so
+  // chunk c (step c of the group) of row j sits at 16 * (4 j + (c ^ ((j >> 1) & 3))).
+  const int h = w & 1, wp = w >> 1;
+  const int n_code = w < 4 ? 4 : 3;
+  const uint32_t lane_c = (uint32_t)(8 * h + (lane >> 3)) * cstride + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+  const uint32_t lane_s = (uint32_t)(lane >> 2) * sstride + 16u * (uint32_t)((lane & 3) ^ ((lane >> 3) & 3));
+  uint32_t coff[kCodeLoadsMax], soff[kScaleLoads];
+  auto set_code_tile = [&](int mb, int nb) {
 #pragma unroll
-  for (int i = 0; i < WTM; ++i)
-#pragma unroll
-    for (int j = 0; j < WTN; ++j) acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Prologue: steps 0 and 1 in flight.  Per step the issue order is (codes,
-  // scales), 2*WT operations; at the top of step i the operations of step
-  // i+1 (issued after step i's) may stay outstanding.  The loop is unrolled
-  // by the ring depth so that every slot (LDS and scale registers) is named
-  // statically: a scale register is never copied while its load is in flight.
-  auto step = [&](int i, const Scales& sc, Scales& sc_next2, uint8_t* slot, uint8_t* slot_next2) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * WT));
-    u4_t code[WT];
-#pragma unroll
-    for (int t = 0; t < WT; ++t) code[t] = *reinterpret_cast<const u4_t*>(slot + t * 1024 + 16 * lane);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * WT) & ~(15 << 8));  // LDS reads of this slot done
-    __builtin_amdgcn_sched_barrier(0);
-    {  // step i + 2 -> the slot and scale registers that step i - 1 used
-      const int i2 = i + 2;
-      const bool ok = i2 < my;
-      const uint32_t co = (uint32_t)(s_begin + i2) * 64, so = (uint32_t)(s_begin + i2) * 8;
-#pragma unroll
-      for (int t = 0; t < WTM; ++t)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ac, LDS_PTR(slot_next2 + t * 1024), 16,
-                                                 ok ? a_c0 + t * tc + co : OOB, 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < WTN; ++t)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wc, LDS_PTR(slot_next2 + (WTM + t) * 1024), 16,
-                                                 ok ? b_c0 + t * tc + co : OOB, 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < WTM; ++t)
-        sc_next2.v[t] = __builtin_amdgcn_raw_buffer_load_b16(as, ok ? a_s0 + t * ts + so : OOB, 0, 0);
-#pragma unroll
-      for (int t = 0; t < WTN; ++t)
-        sc_next2.v[WTM + t] = __builtin_amdgcn_raw_buffer_load_b16(ws, ok ? b_s0 + t * ts + so : OOB, 0, 0);
+    for (int k = 0; k < kCodeLoadsMax; ++k) {
+      const int t = wp + 4 * k;
+      const int row = t < TA ? mb + 16 * t : nb + 16 * (t - TA);
+      coff[k] = (uint32_t)row * cstride + lane_c;
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (i < my) {
-      h2_t sp[WT];  // the two block scales of every tile, converted once per step
+  };
+  auto set_scale_tile = [&](int mb, int nb) {
 #pragma unroll
-      for (int t = 0; t < WT; ++t) sp[t] = e4m3x2_to_h2(sc.v[t]);
+    for (int k = 0; k < kScaleLoads; ++k) {
+      const int t = min(w + 8 * k, TT - 1);
+      const int row = t < TA ? mb + 16 * t : nb + 16 * (t - TA);
+      soff[k] = (uint32_t)row * sstride + lane_s;
+    }
+  };
+  auto issue_codes = [&](int i, int slot) {
+    uint8_t* base = lds + slot * kSlotBytes + h * 1024;
+    const uint32_t so = (uint32_t)i * 128u;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        h8_t bf[WTN];
+    for (int k = 0; k < kCodeLoadsMax; ++k)
+      if (k < 3 || w < 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(k == 0 ? rac : rwc, LDS_PTR(base + (wp + 4 * k) * kTileStep), 16,
+                                                 coff[k] + so, 0, 0, 0);
+  };
+  auto issue_scales = [&](int gi, int buf) {
+    uint8_t* base = lds + kScaleOff + buf * kScaleBuf;
+    const uint32_t so = (uint32_t)gi * 64u;
 #pragma unroll
-        for (int j = 0; j < WTN; ++j) bf[j] = dequant8(code[WTM + j][kk], sp[WTM + j][kk >> 1]);
+    for (int k = 0; k < kScaleLoads; ++k) {
+      const int t = min(w + 8 * k, TT - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(t < TA ? ras : rws, LDS_PTR(base + t * kScaleTile), 16,
+                                               soff[k] + so, 0, 0, 0);
+    }
+  };
+
+  // Consumer side: lane (r32, kq) of wave w takes the 8 code bytes
+  // [16w + 8kq, 16w + 8kq + 8) of row r32 of every 32-row MFMA tile, i.e.
+  // K = 32w + 16kq + 0..15 of the step: one 16-block, whose scale is byte
+  // 2w + kq of the step's 16.  Its first dword feeds slice 0 (one MFMA), the
+  // second slice 1 (the same permutation of K on both operands, so the sum is
+  // unchanged).  MFMA tile t of the workgroup (0-1 A, 2-6 B) is load tiles 2t
+  // and 2t + 1.
+  const int jr = r32 & 15;
+  const int rd_code = kTileStep * (r32 >> 4) + 128 * jr + 16 * (w ^ (jr & 7)) + 8 * kq;
+  const int rd_scale = kScaleTile * (r32 >> 4) + 64 * jr + 2 * w + kq;
+  const int sw_r = (jr >> 1) & 3;
+  struct Ops {
+    u2_t c[FT];
+    uint32_t s[FT];
+  };
+  auto read_ops = [&](int slot, int buf, int i, Ops& o) {
+    const uint8_t* cs = lds + slot * kSlotBytes + rd_code;
+    const uint8_t* ss = lds + kScaleOff + buf * kScaleBuf + rd_scale + 16 * ((i & 3) ^ sw_r);
 #pragma unroll
-        for (int ti = 0; ti < WTM; ++ti) {
-          const h8_t af = dequant8(code[ti][kk], sp[ti][kk >> 1]);
+    for (int t = 0; t < FT; ++t) o.c[t] = *reinterpret_cast<const u2_t*>(cs + t * 2 * kTileStep);
 #pragma unroll
-          for (int j = 0; j < WTN; ++j) acc[ti][j] = mfma16x16x32(af, bf[j], acc[ti][j]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int t = 0; t < FT; ++t) o.s[t] = ss[t * 2 * kScaleTile];
+  };
+  auto multiply = [&](const Ops& o, f32x16_t (&acc)[MT][NT]) {
+    _Float16 sv[FT];
+#pragma unroll
+    for (int t = 0; t < FT; ++t) sv[t] = (_Float16)e4m3_to_f32(o.s[t]);
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      h8_t af[MT];
+#pragma unroll
+      for (int ti = 0; ti < MT; ++ti) af[ti] = dequant8(o.c[ti][sl], sv[ti]);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const h8_t bf = dequant8(o.c[MT + j][sl], sv[MT + j]);
+#pragma unroll
+        for (int ti = 0; ti < MT; ++ti) acc[ti][j] = mfma32x32x16(af[ti], bf, acc[ti][j]);
       }
     }
   };
 
-  uint8_t* slot0 = ring;
-  uint8_t* slot1 = ring + kSlotBytes;
-  uint8_t* slot2 = ring + 2 * kSlotBytes;
-  Scales sc0, sc1, sc2;
-  dma_step(0);
-  sc0 = load_scales(0);
-  dma_step(1);
-  sc1 = load_scales(1);
-  for (int i0 = 0; i0 < my; i0 += 3) {
-    step(i0, sc0, sc2, slot0, slot2);
-    step(i0 + 1, sc1, sc0, slot1, slot0);
-    step(i0 + 2, sc2, sc1, slot2, slot1);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // every wave is done with its ring; the LDS is reused below
-
-  // Reduction of the four K-quarters, in phases of two A tiles (32 rows):
-  // every wave dumps its 2 x 5 accumulator tiles (lane-major), then wave w
-  // adds tiles p = w, w+4, w+8 of the phase over waves 0..3 in order and
-  // stores them.
-  f4_t* red_lds = reinterpret_cast<f4_t*>(wt_lds);
   const float gg = (*p.ga) * (*p.gw);
+
+  // Load pointers: codes run three steps ahead of the multiplies, scales one
+  // group ahead; both continue into the next tile.
+  int c_it = 0, c_i = 0, s_it = 0, s_gi = 0;
+  bool s_valid = true;
+  auto advance_codes = [&]() {
+    if (++c_i == steps) {
+      c_i = 0;
+      if (++c_it < my_tiles) {
+        int mb, nb;
+        coords(c_it, mb, nb);
+        set_code_tile(mb, nb);
+      }
+    }
+  };
+  auto advance_scales = [&]() {
+    if (++s_gi == groups) {
+      s_gi = 0;
+      if (++s_it < my_tiles) {
+        int mb, nb;
+        coords(s_it, mb, nb);
+        set_scale_tile(mb, nb);
+      } else {
+        s_valid = false;
+      }
+    }
+  };
+
+  // Loads issued (by this wave) after the codes of the step the next wait is
+  // for: the scale group issued with them, and the codes and scales of the
+  // step after.  With every group 4 steps long, a step's scale group was
+  // issued before its codes.
+  int c_prev1 = 0, s_prev1 = 0, s_prev2 = 0;
+  Ops opa, opb;
+  {
+    int mb, nb;
+    coords(0, mb, nb);
+    set_code_tile(mb, nb);
+    set_scale_tile(mb, nb);
+    issue_scales(0, 0);
+    advance_scales();
+    const int n_pro = total_steps < 3 ? total_steps : 3;
+    for (int j = 0; j < n_pro; ++j) {
+      issue_codes(c_i, j);
+      advance_codes();
+    }
+    wait_vm(n_code * (n_pro - 1));
+    barrier_lds();
+    read_ops(0, 0, 0, opa);
+    c_prev1 = n_pro == 3 ? n_code : 0;
+  }
+
+  // Top of step g: make step g + 1's operands ready in `nxt` and keep the
+  // loads three steps ahead.  i is g's index inside its tile, it its tile.
+  int slot = 0, sb = 0, g = 0;
+  auto advance = [&](int i, int it, Ops& nxt) {
+    const int ni = (i + 1 == steps) ? 0 : i + 1;
+    const int nslot = slot == 2 ? 0 : slot + 1;
+    const int nsb = (ni & 3) == 0 ? sb ^ 1 : sb;
+    if (g + 1 < total_steps) {
+      // After a tile's epilogue its output stores are outstanding too: wait for all.
+      wait_vm(i == 0 && it > 0 ? 0 : s_prev2 + c_prev1 + s_prev1);
+      barrier_lds();
+      read_ops(nslot, nsb, ni, nxt);
+      int c_cur = 0, s_cur = 0;
+      if (g + 3 < total_steps) {
+        issue_codes(c_i, slot);
+        advance_codes();
+        c_cur = n_code;
+      }
+      if ((i & 3) == 0 && s_valid) {
+        issue_scales(s_gi, sb ^ 1);
+        advance_scales();
+        s_cur = kScaleLoads;
+      }
+      s_prev2 = s_prev1;
+      s_prev1 = s_cur;
+      c_prev1 = c_cur;
+    }
+    slot = nslot;
+    sb = nsb;
+    ++g;
+  };
+
+  for (int it = 0; it < my_tiles; ++it) {
+    int m0, n0;
+    coords(it, m0, n0);
+    f32x16_t acc[MT][NT];
 #pragma unroll
-  for (int ph = 0; ph < WTM / 2; ++ph) {
+    for (int ti = 0; ti < MT; ++ti)
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int j = 0; j < WTN; ++j)
-        red_lds[((wave * 2 + ii) * WTN + j) * 64 + lane] = acc[2 * ph + ii][j];
-    __syncthreads();
-    for (int pidx = wave; pidx < 2 * WTN; pidx += WKS) {
-      const int ii = pidx / WTN, j = pidx % WTN;
-      f4_t sum = red_lds[((0 * 2 + ii) * WTN + j) * 64 + lane];
+        for (int e = 0; e < 16; ++e) acc[ti][j][e] = 0.0f;
+
+    // steps is even: every tile starts with its operands in opa
+    for (int i = 0; i < steps; i += 2) {
+      advance(i, it, opb);
+      __builtin_amdgcn_sched_barrier(0);
+      multiply(opa, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      advance(i + 1, it, opa);
+      __builtin_amdgcn_sched_barrier(0);
+      multiply(opb, acc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Tile done: reduce the eight K-eighths one accumulator tile at a time.
+    // Every wave dumps its tile (element pair e2 of lane l at
+    // (w * 8 + e2) * 64 + l), then wave w adds pair e2 = w over waves 0..7 in
+    // order and stores it: elements 2w, 2w + 1 of lane l are rows
+    // 8(w / 2) + 4(l / 32) + 2(w % 2) + 0..1, column l % 32 of the tile.
+    f2_t* red = reinterpret_cast<f2_t*>(lds + kRedOff);
 #pragma unroll
-      for (int w = 1; w < WKS; ++w) sum += red_lds[((w * 2 + ii) * WTN + j) * 64 + lane];
-      const int n = n0 + 16 * j + r;
+    for (int tix = 0; tix < MT * NT; ++tix) {
+      const f32x16_t a = acc[tix / NT][tix % NT];
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) red[(w * 8 + e2) * 64 + lane] = f2_t{a[2 * e2], a[2 * e2 + 1]};
+      barrier_lds();
+      f2_t sum = red[(0 * 8 + w) * 64 + lane];
+#pragma unroll
+      for (int v = 1; v < kWaves; ++v) sum += red[(v * 8 + w) * 64 + lane];
+      const int n = n0 + 32 * (tix % NT) + r32;
       if (n < N) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = m0 + 16 * (2 * ph + ii) + 4 * q + e;
+        for (int e = 0; e < 2; ++e) {
+          const int m = m0 + 32 * (tix / NT) + 8 * (w >> 1) + 4 * kq + 2 * (w & 1) + e;
           if (m < M) {
             const float v = sum[e] * gg;
             const int64_t o = (int64_t)m * N + n;
@@ -364,30 +500,45 @@ __global__ __launch_bounds__(64 * WKS) void gemm_wave_tiled_kernel(GemmArgs p, i
           }
         }
       }
+      barrier_lds();
     }
-    __syncthreads();
   }
 }
 
 }  // namespace
 
+static int tiled_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
-  if (a.K % 128 == 0 && a.K >= 128 * WKS) {
-    const int tiles_m = (a.M + 16 * WTM - 1) / (16 * WTM), tiles_n = (a.N + 16 * WTN - 1) / (16 * WTN);
-    const size_t lds = (size_t)WKS * kWaveLds;  // >= the reduction buffer (WKS * 2 * WTN KiB)
-    const dim3 grid((unsigned)(tiles_m * tiles_n));
+  // buffer offsets are 32-bit: rows up to one tile past the end must stay below 2^31 bytes
+  const int64_t rows = (int64_t)(a.M > a.N ? a.M : a.N) + BNW;
+  if (a.K % (kStepK * kGroup) == 0 && a.K > 0 && rows * (a.K / 2) < ((int64_t)1 << 31)) {
+    const int tiles_m = (a.M + BMW - 1) / BMW, tiles_n = (a.N + BNW - 1) / BNW;
+    const int total = tiles_m * tiles_n;
+    const int cus = tiled_cus();
+    const dim3 grid((unsigned)(total < cus ? total : cus));
     // more than the default 64 KiB of dynamic LDS: raise the kernels' limit once
     static const hipError_t attr = [] {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wave_tiled_kernel<true>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, WKS * kWaveLds);
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wg_tiled_kernel<true>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
       if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wave_tiled_kernel<false>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, WKS * kWaveLds);
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wg_tiled_kernel<false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
       return e;
     }();
     if (attr != hipSuccess) return attr;
-    if (a.out_bf16) gemm_wave_tiled_kernel<true><<<grid, 64 * WKS, lds, stream>>>(a, tiles_m, tiles_n);
-    else gemm_wave_tiled_kernel<false><<<grid, 64 * WKS, lds, stream>>>(a, tiles_m, tiles_n);
+    if (a.out_bf16) gemm_wg_tiled_kernel<true><<<grid, 64 * kWaves, kLdsBytes, stream>>>(a, tiles_m, tiles_n);
+    else gemm_wg_tiled_kernel<false><<<grid, 64 * kWaves, kLdsBytes, stream>>>(a, tiles_m, tiles_n);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));

@@ -67,6 +67,27 @@ def test_gemm_small_shapes_all_paths(M, K, N):
                         f"M={M} K={K} N={N} path={path} {out_dtype}")
 
 
+# The persistent tiled kernel (K % 1024 == 0, M > 16): 128 x 80 tiles, 256-K steps, scale bytes
+# fetched four steps at a time, loads three steps ahead across tile boundaries.  Cases: one scale
+# group, ragged M and N, more tiles than workgroups (600 and 262 tiles: several tiles per
+# workgroup, with and without a tile count divisible by 8), a single tile, M just above 16.  K %
+# 256 == 0 shapes outside that rule (768, 1280) take the simple tiled kernel.
+TILED_CASES = [(129, 1024, 300), (200, 2048, 1000), (300, 3072, 16000), (129, 1024, 10480), (512, 4096, 80),
+               (17, 1024, 2000), (129, 768, 300), (200, 1280, 1000)]
+
+
+@pytest.mark.parametrize("M,K,N", TILED_CASES)
+def test_gemm_tiled_persistent(M, K, N):
+    rng = np.random.default_rng(7 * M + K + N)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    dev, ref = _quantized_pair(A, W)
+    C, T = _oracle(ref)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        out = B.nvfp4_gemm(*dev, out_dtype=out_dtype, path=B.PATH_TILED)
+        U.assert_within(U.host(out), C, T + U.out_rounding_slack(C, out_dtype), f"M={M} K={K} N={N} {out_dtype}")
+
+
 # One or two activation rows with K >= 2048 and K % 256 == 0 take the memory-order GEMV: rows
 # whose chunk count (K/32) is not a multiple of 64, row runs that wrap inside an instruction,
 # several rows per wave (N above the resident wave count), a single row; K = 2080 (odd chunk
