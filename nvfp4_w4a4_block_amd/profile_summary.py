@@ -1,13 +1,14 @@
 """Summaries of rocprofv3 runs of bench.py, as committed under profiles/.
 
     python -m nvfp4_w4a4_block_amd.profile_summary trace <kernel_stats.csv> <out.md> \
-        --title TEXT --command TEXT [--bytes B --kernel SUBSTR]
+        --title TEXT --command TEXT [--bytes B | --flops F [--peak-tflops P]] [--kernel SUBSTR]
     python -m nvfp4_w4a4_block_amd.profile_summary traffic <fetch.csv> <write.csv> <out.json> \
         --kernel SUBSTR --sources FILE... --command TEXT --command TEXT [--copy-mib 128]
 
 `trace` turns the per-kernel statistics of `rocprofv3 --kernel-trace --stats
 --output-format csv` into a markdown table (and, with --bytes, the achieved
-GB/s of the named kernel).  `traffic` reads two `rocprofv3 --pmc FETCH_SIZE`
+GB/s of the named kernel, or with --flops its TFLOP/s against a matrix-core
+peak).  `traffic` reads two `rocprofv3 --pmc FETCH_SIZE`
 / `--pmc WRITE_SIZE` counter files of a bench run made with
 --copy-reference-mib, scales each counter by what it reads for that plain copy
 of known size (the last three copy dispatches), and writes the HBM bytes per
@@ -46,6 +47,14 @@ def trace(args) -> None:
             out += [f"Algorithmic bytes per launch of `{args.kernel}`: {args.bytes:,}; "
                     f"average {avg:,.1f} ns -> {args.bytes / avg:,.1f} GB/s "
                     f"({100 * args.bytes / avg / 8000:.1f}% of 8 TB/s).", ""]
+    if args.flops and args.kernel:
+        k = [r for r in rows if args.kernel in r["Name"]]
+        if k:
+            avg = float(k[0]["AverageNs"])
+            tf = args.flops / avg / 1e3
+            out += [f"Algorithmic flops per launch of `{args.kernel}`: {args.flops:,}; "
+                    f"average {avg:,.1f} ns -> {tf:,.1f} TFLOP/s "
+                    f"({100 * tf / args.peak_tflops:.1f}% of {args.peak_tflops:,.0f} TFLOP/s).", ""]
     out += ["| Name | Calls | Total (ns) | Average (ns) | Percent | Min (ns) | Max (ns) |",
             "| :-- | --: | --: | --: | --: | --: | --: |"]
     for r in rows:
@@ -104,6 +113,8 @@ def main() -> None:
     t.add_argument("--title", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--bytes", type=int, default=0)
+    t.add_argument("--flops", type=int, default=0)
+    t.add_argument("--peak-tflops", type=float, default=2500.0)
     t.add_argument("--kernel", default="")
     r = sub.add_parser("traffic")
     r.add_argument("fetch")
