@@ -92,6 +92,9 @@ class Pipeline:
         self.as1 = torch.empty((M, K // 16), dtype=torch.uint8, device=DEV)
         self.out_dtype = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
         self.y1 = torch.empty((M, N), dtype=self.out_dtype, device=DEV)
+        # 3..16 rows: the workspace with which the GEMM splits a long K over workgroups (None
+        # when it needs none); zeroed once, left zeroed by every call
+        self.split_ws = B.gemm_workspace(M, K, N, torch.device(DEV)) if 3 <= M <= 16 else None
         self.tree = wl.name == "tree_verify"
         if self.tree:  # 16 nodes over 8 depths: a main chain plus one alternative per depth
             parent, chain = [-1], [0]
@@ -118,6 +121,11 @@ class Pipeline:
         wc, ws, gw = self.l1.copies[i % self.R]
         if self.dynamic_scale:
             B.nvfp4_act_global_scale(self.a, out=self.g1)
+        if self.split_ws is not None:  # quantization, then the GEMM with its K split over workgroups
+            B.nvfp4_quantize_act(self.a, self.g1, self.ac1, self.as1)
+            B.nvfp4_gemm(self.ac1, self.as1, self.g1, wc, ws, gw, out_dtype=self.out_dtype, out=self.y1,
+                         workspace=self.split_ws)
+            return
         B.nvfp4_quantize_gemm(self.a, self.g1, wc, ws, gw, out_dtype=self.out_dtype, out=self.y1,
                               a_codes=self.ac1, a_scales=self.as1)
 
@@ -157,7 +165,8 @@ class Pipeline:
             self._gemm1(i)
             return
         wc, ws, gw = self.l1.copies[i % self.R]
-        B.nvfp4_gemm(self.ac1, self.as1, self.g1, wc, ws, gw, out_dtype=self.out_dtype, out=self.y1)
+        B.nvfp4_gemm(self.ac1, self.as1, self.g1, wc, ws, gw, out_dtype=self.out_dtype, out=self.y1,
+                     workspace=self.split_ws)
 
 
 def capture(fn, count: int) -> torch.cuda.CUDAGraph:
@@ -339,7 +348,8 @@ def main() -> int:
     step_ms = timed_replays(step_graphs, K, P.R) / K
     kern_ms = timed_replays(gemm_graphs, K, P.R) / K
     kname = ("LM head + fused argmax + tree acceptance" if P.tree else
-             "fused quantize + FP4 GEMV" if P.fused_single_kernel else "first GEMM")
+             "fused quantize + FP4 GEMV" if P.fused_single_kernel else
+             "M<=16 weight-streaming GEMM (gemm_m16_kernel)" if 3 <= wl.M <= 16 else "first GEMM")
     log(f"[bench] step {step_ms * 1e3:.2f} us, {kname} {kern_ms * 1e3:.2f} us per launch")
 
     if wl.chain:

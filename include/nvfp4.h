@@ -147,6 +147,39 @@ nvfp4_status nvfp4_gemm_ex(int64_t M, int64_t K, int64_t N,
                            const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
                            void* out, nvfp4_dtype out_dt, int path, void* stream);
 
+/* Size in bytes of the workspace with which nvfp4_gemm_ws splits the
+ * contraction of an (M, K, N) product over several workgroups; 0 when it
+ * would not (M outside 3..16, K not a multiple of 128, or enough rows to fill
+ * the GPU without a split).  Depends only on (M, K, N) and the device's
+ * compute-unit count.  At the tree-verification pass of a down-projection
+ * (M = 16, K = 25600, N = 5120) it is a few MiB.
+ * Cites: the section on tree-based multi-token prediction (one pass over the
+ * 16 candidates: few output rows, a long contraction). */
+int64_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/* nvfp4_gemm with a caller-owned workspace; same arguments and result
+ * contract as nvfp4_gemm.
+ *   workspace        device memory, 16-byte aligned, or NULL with
+ *                    workspace_bytes == 0 (then exactly nvfp4_gemm).
+ *   workspace_bytes  its size.  With at least nvfp4_gemm_workspace_bytes(M,
+ *                    K, N) bytes the product splits K over workgroups, each
+ *                    writing fp32 partial sums there; the last workgroup of
+ *                    a row block to finish adds them in a fixed order, so the
+ *                    result is still bit-identical from run to run.  A
+ *                    smaller workspace runs the unsplit kernels.
+ * The workspace must be all zero before its first use (its leading counters
+ * must read zero on entry); every call leaves them zero again, so it is
+ * cleared once, not per call.  Calls sharing a workspace must be ordered on
+ * one stream.  Errors: workspace_bytes < 0 -> NVFP4_ERR_SHAPE; NULL with
+ * workspace_bytes > 0 -> NVFP4_ERR_NULL; misaligned -> NVFP4_ERR_ALIGN.
+ * Cites: the sections on NVFP4 quantization and tree-based multi-token
+ * prediction. */
+nvfp4_status nvfp4_gemm_ws(int64_t M, int64_t K, int64_t N,
+                           const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                           void* out, nvfp4_dtype out_dt, void* workspace, int64_t workspace_bytes,
+                           void* stream);
+
 /* Activation quantization and GEMM in one call: the decode step's
  * nvfp4_quantize_act + nvfp4_gemm.
  *   a         [M][K] raw activations in a_dt (NVFP4_F32 or NVFP4_BF16), device.
@@ -212,8 +245,8 @@ nvfp4_status nvfp4_tree_accept(int64_t n_nodes, const int32_t* parent, const int
  *   M        1..16 tree nodes (rows); K, N (vocabulary): as nvfp4_gemm, with the
  *            nodes' NVFP4 activations a_* and the LM-head weights w_*.
  *   parent, draft: as nvfp4_tree_accept.
- *   logits   optional out [M][N] fp32 (may be NULL when K % 256 == 0 and
- *            K <= 5120: the argmax is then fused into the GEMM and the logits
+ *   logits   optional out [M][N] fp32 (may be NULL when K % 128 == 0 and
+ *            K <= 7168: the argmax is then fused into the GEMM and the logits
  *            are not written; other K need it).
  *   greedy   out [M] int32: each row's argmax (lowest column on ties; -0.0
  *            orders just below +0.0).

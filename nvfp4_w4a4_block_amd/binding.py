@@ -22,7 +22,8 @@ NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_DTYPE, NVF
 NVFP4_F32, NVFP4_BF16 = 0, 1
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 
-EXPORTS = ("nvfp4_abi_version", "nvfp4_act_global_scale", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_kv_fp8_decode", "nvfp4_kv_fp8_encode",
+EXPORTS = ("nvfp4_abi_version", "nvfp4_act_global_scale", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_gemm_workspace_bytes",
+           "nvfp4_gemm_ws", "nvfp4_kv_fp8_decode", "nvfp4_kv_fp8_encode",
            "nvfp4_quantize_act",
            "nvfp4_quantize_gemm", "nvfp4_quantize_weights", "nvfp4_status_string", "nvfp4_tree_accept",
            "nvfp4_tree_verify")
@@ -49,13 +50,16 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_quantize_act.argtypes = [p, i32, i64, i64, p, p, p, p]
     lib.nvfp4_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, p]
     lib.nvfp4_gemm_ex.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, i32, p]
+    lib.nvfp4_gemm_ws.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, p, i64, p]
+    lib.nvfp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.nvfp4_gemm_workspace_bytes.restype = i64
     lib.nvfp4_quantize_gemm.argtypes = [i64, i64, i64, p, i32, p, p, p, p, p, i32, p, p, p]
     lib.nvfp4_tree_accept.argtypes = [i64, p, p, p, p, p]
     lib.nvfp4_kv_fp8_encode.argtypes = [p, i32, i64, p, p, p]
     lib.nvfp4_act_global_scale.argtypes = [p, i32, i64, i64, p, p]
     lib.nvfp4_kv_fp8_decode.argtypes = [p, i64, p, p, i32, p]
     lib.nvfp4_tree_verify.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p, p, p, p, p, p]
-    for f in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "nvfp4_gemm", "nvfp4_gemm_ex",
+    for f in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_gemm_ws",
               "nvfp4_quantize_gemm", "nvfp4_tree_accept", "nvfp4_tree_verify", "nvfp4_kv_fp8_encode",
               "nvfp4_kv_fp8_decode", "nvfp4_act_global_scale"):
         getattr(lib, f).restype = i32
@@ -136,11 +140,30 @@ def nvfp4_quantize_act(a: torch.Tensor, g_a: torch.Tensor, codes: Optional[torch
     return codes, scales
 
 
+_gemm_workspaces: dict = {}
+
+
+def gemm_workspace(M: int, K: int, N: int, dev: torch.device) -> Optional[torch.Tensor]:
+    """A zeroed workspace of at least nvfp4_gemm_workspace_bytes(M, K, N) bytes on `dev`, or None
+    when the product needs none.  Cached per device and grown when too small; every call leaves
+    its counters zero, so it is zeroed only when allocated.  Shared by the calls of this module:
+    keep them on one stream, or pass a workspace of your own."""
+    need = int(load().nvfp4_gemm_workspace_bytes(M, K, N))
+    if need <= 0:
+        return None
+    ws = _gemm_workspaces.get(dev)
+    if ws is None or ws.numel() < need:
+        ws = _gemm_workspaces[dev] = torch.zeros((need,), dtype=torch.uint8, device=dev)
+    return ws
+
+
 def nvfp4_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: torch.Tensor,
                w_codes: torch.Tensor, w_scales: torch.Tensor, g_w: torch.Tensor,
                out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
-               path: int = PATH_AUTO) -> torch.Tensor:
-    """NVFP4 W4A4 product: out [M, N] = dequant(A) @ dequant(W)^T, fp32 accumulation."""
+               path: int = PATH_AUTO, workspace=None) -> torch.Tensor:
+    """NVFP4 W4A4 product: out [M, N] = dequant(A) @ dequant(W)^T, fp32 accumulation.
+    workspace: None (nvfp4_gemm_ex with `path`), "auto" (gemm_workspace(), nvfp4_gemm_ws) or a
+    uint8 device tensor (nvfp4_gemm_ws; zero before its first use)."""
     if a_codes.dim() != 2 or w_codes.dim() != 2:
         raise ValueError("codes must be 2-D")
     M, K2 = a_codes.shape
@@ -160,10 +183,27 @@ def nvfp4_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: torch.Tensor,
     elif out.shape != (M, N) or out.dtype != out_dtype:
         raise ValueError("out must be [M, N] of out_dtype")
     _dev(a_codes, out)
-    _check(load().nvfp4_gemm_ex(M, K, N, a_codes.data_ptr(), a_scales.data_ptr(), g_a.data_ptr(),
+    if workspace is None:
+        _check(load().nvfp4_gemm_ex(M, K, N, a_codes.data_ptr(), a_scales.data_ptr(), g_a.data_ptr(),
+                                    w_codes.data_ptr(), w_scales.data_ptr(), g_w.data_ptr(),
+                                    out.data_ptr(), _dt(out_dtype), path, _stream(dev)),
+               "nvfp4_gemm")
+        return out
+    if path != PATH_AUTO:
+        raise ValueError("a workspace is used by the automatic path only")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be None, "auto" or a uint8 tensor')
+        workspace = gemm_workspace(M, K, N, dev)
+    if workspace is not None and (workspace.dtype != torch.uint8 or workspace.device != dev or
+                                  not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor on the operands' device")
+    _check(load().nvfp4_gemm_ws(M, K, N, a_codes.data_ptr(), a_scales.data_ptr(), g_a.data_ptr(),
                                 w_codes.data_ptr(), w_scales.data_ptr(), g_w.data_ptr(),
-                                out.data_ptr(), _dt(out_dtype), path, _stream(dev)),
-           "nvfp4_gemm")
+                                out.data_ptr(), _dt(out_dtype),
+                                workspace.data_ptr() if workspace is not None else None,
+                                workspace.numel() if workspace is not None else 0, _stream(dev)),
+           "nvfp4_gemm_ws")
     return out
 
 

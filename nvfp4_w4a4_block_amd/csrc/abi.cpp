@@ -41,7 +41,7 @@ const char* nvfp4_status_string(nvfp4_status s) {
   return "unknown status";
 }
 
-int nvfp4_abi_version(void) { return 5; }
+int nvfp4_abi_version(void) { return 6; }
 
 nvfp4_status nvfp4_quantize_weights(const void* w, nvfp4_dtype w_dt, int64_t N, int64_t K,
                                     uint8_t* w_codes, uint8_t* w_scales, float* w_global,
@@ -87,23 +87,32 @@ nvfp4_status nvfp4_quantize_act(const void* a, nvfp4_dtype a_dt, int64_t M, int6
                                          static_cast<hipStream_t>(stream)));
 }
 
-nvfp4_status nvfp4_gemm_ex(int64_t M, int64_t K, int64_t N,
-                           const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
-                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
-                           void* out, nvfp4_dtype out_dt, int path, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// nvfp4_gemm_ex / nvfp4_gemm_ws: validation, then the chosen path.
+nvfp4_status gemm_impl(int64_t M, int64_t K, int64_t N,
+                       const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                       void* out, nvfp4_dtype out_dt, int path, void* workspace, int64_t workspace_bytes,
+                       void* stream) {
   if (!dtype_ok(out_dt)) return NVFP4_ERR_DTYPE;
   if (path != NVFP4_PATH_AUTO && path != NVFP4_PATH_SKINNY && path != NVFP4_PATH_TILED)
     return NVFP4_ERR_DTYPE;
   if (!shape_ok(M, K) || !shape_ok(N, K)) return NVFP4_ERR_SHAPE;
   if (M > 0 && N >= kMaxElems / M) return NVFP4_ERR_SHAPE;
+  if (workspace_bytes < 0) return NVFP4_ERR_SHAPE;
   if (path == NVFP4_PATH_AUTO) path = M <= 16 ? NVFP4_PATH_SKINNY : NVFP4_PATH_TILED;
   if ((path == NVFP4_PATH_SKINNY ? (M + 15) / 16 : (M + 127) / 128) > kMaxGridY)
     return NVFP4_ERR_SHAPE;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!a_codes || !a_scales || !a_global || !w_codes || !w_scales || !w_global || !out)
     return NVFP4_ERR_NULL;
+  if (workspace_bytes > 0 && !workspace) return NVFP4_ERR_NULL;
   if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) ||
-      !aligned16(w_scales) || !aligned16(out) || !aligned4(a_global) || !aligned4(w_global))
+      !aligned16(w_scales) || !aligned16(out) || !aligned4(a_global) || !aligned4(w_global) ||
+      (workspace && !aligned16(workspace)))
     return NVFP4_ERR_ALIGN;
   nvfp4::GemmArgs g;
   g.M = (int)M;
@@ -117,9 +126,41 @@ nvfp4_status nvfp4_gemm_ex(int64_t M, int64_t K, int64_t N,
   g.gw = w_global;
   g.out = out;
   g.out_bf16 = out_dt == NVFP4_BF16;
+  g.workspace = workspace_bytes > 0 ? workspace : nullptr;
+  g.workspace_bytes = workspace_bytes;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return from_hip(path == NVFP4_PATH_SKINNY ? nvfp4::launch_gemm_skinny(g, s)
                                             : nvfp4::launch_gemm_tiled(g, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_gemm_ex(int64_t M, int64_t K, int64_t N,
+                           const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                           void* out, nvfp4_dtype out_dt, int path, void* stream) {
+  return gemm_impl(M, K, N, a_codes, a_scales, a_global, w_codes, w_scales, w_global, out, out_dt, path,
+                   nullptr, 0, stream);
+}
+
+int64_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  if (M < 3 || M > 16 || !shape_ok(M, K) || !shape_ok(N, K) || N < 1 || N >= kMaxElems / M) return 0;
+  nvfp4::GemmArgs g;
+  g.M = (int)M;
+  g.K = (int)K;
+  g.N = (int)N;
+  return nvfp4::gemm_m16_workspace_bytes(g);
+}
+
+nvfp4_status nvfp4_gemm_ws(int64_t M, int64_t K, int64_t N,
+                           const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                           void* out, nvfp4_dtype out_dt, void* workspace, int64_t workspace_bytes,
+                           void* stream) {
+  return gemm_impl(M, K, N, a_codes, a_scales, a_global, w_codes, w_scales, w_global, out, out_dt,
+                   NVFP4_PATH_AUTO, workspace, workspace_bytes, stream);
 }
 
 nvfp4_status nvfp4_quantize_gemm(int64_t M, int64_t K, int64_t N,

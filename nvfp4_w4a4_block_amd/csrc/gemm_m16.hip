@@ -1,30 +1,39 @@
-// Weight-streaming GEMM for 3 to 16 activation rows: the verification pass of
-// a 16-node candidate tree and the language-model head over it (page
+// Weight-streaming GEMM for up to 16 activation rows: the verification pass
+// of a 16-node candidate tree, and the language-model head over it (page
 // "TensorRT Edge-LLM Completes the MLPerf Edge Agentic Benchmark 6.4x Faster
 // on Jetson AGX Thor", sections "Using tree-based multi-token prediction to
 // accelerate LLM inference" and "Using NVFP4 quantization to accelerate
-// Qwen3.6-27B inference").  At these sizes the product still reads every
-// weight once and little else, so the kernel is built like the FP4 GEMV:
+// Qwen3.6-27B inference").  At these sizes the product reads every weight
+// once and little else, so the kernel is a weight stream feeding f16 matrix
+// cores:
 //
-//   - one 16-byte load per lane covers 8 weight rows x 128 bytes (a 256-element
-//     line of each): lane j + 16q holds bytes 64(j%2) + 16q .. +15 of row j/2;
+//   - a line is 128 K-elements: 64 code bytes and 8 scale bytes of a row;
+//   - one 16-byte load per lane covers a line of 16 weight rows: lane
+//     j + 16q holds bytes 16q .. 16q+15 of row j's line (elements 32q ..
+//     32q+31, blocks 2q and 2q+1), a 64-byte run per row;
 //   - the codes are dequantized exactly to f16 with their E4M3 scale (E2M1 x
 //     E4M3 has at most 6 significant bits and lies in [2^-10, 2688]) and are
-//     the B operand of v_mfma_f32_16x16x32_f16: column j = (row j/2, half j%2);
-//   - the A operand is the 16 activation rows (rows past M read zeros), staged
-//     once per workgroup in LDS as codes and scales and dequantized exactly to
-//     f16 the same way, line by line; lane i + 16q of the MFMA for piece p and
-//     half h holds k = 128h + 32q + 8p .. +7 of activation row i.  Columns of
-//     half h meet their own k there, so the MFMA of half h is kept for the
-//     columns j with j%2 == h (the other columns are unused cross terms);
-//     every product is exact and the fp32 accumulation is the only rounding.
+//     the B operand of v_mfma_f32_16x16x32_f16, column j = weight row j.  For
+//     piece p (elements 32q + 8p .. +7 of every lane) the MFMA's k = 8q + e
+//     is element 32q + 8p + e, so four MFMAs cover the line and every column
+//     of every MFMA is used;
+//   - the A operand is the 16 activation rows (rows past M read zeros), laid
+//     out the same way (lane i + 16q: row i, elements 32q .. 32q+31), staged
+//     once per workgroup in LDS as codes and scales for the workgroup's K
+//     range and dequantized per line, once for the G row groups of a wave.
+//     Every product is exact; the fp32 accumulation is the only rounding.
 //
-// Each wave walks its K range line by line (three lines of weight loads in
-// flight) and, per line, dequantizes the activation operand once for G groups
-// of 8 rows.  K may be split over the KS (<= 8) waves of a workgroup, whose
-// partial sums are added through LDS in a fixed order (results do not depend
-// on timing); nothing is written outside the output.  The staged activations
-// bound K (about 5K); longer K is served by the other skinny kernels.
+// Work split: a workgroup has RB x KS waves; each wave owns G groups of 16
+// rows and one of KS slices of the workgroup's lines, with D lines of weight
+// loads in flight.  The KS partial sums are added through LDS in a fixed
+// order.  When K is long and N small (tree verification of a down-
+// projection: N = 5120 rows, K = 25600) the lines are also split over KZ
+// workgroups (grid.y): each writes its fp32 partial tile to a caller-owned
+// workspace, and the last of the KZ workgroups of a row block to arrive (a
+// counter per row block) adds the KZ partials in the order kz = 0, 1, ... and
+// writes the result, then resets the counter to zero.  The sum does not
+// depend on which workgroup arrives last, so results are bit-identical from
+// run to run.
 #include "device_common.h"
 #include "launch.h"
 
@@ -32,36 +41,63 @@ namespace nvfp4 {
 namespace {
 
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past any array: loads read zeros
-constexpr int kFillMax = 16;            // staged-activation pieces per thread (checked on the host)
+constexpr int kLine = 128;              // K-elements per line
+constexpr int kMaxLdsM16 = 64 * 1024;   // LDS budget of one workgroup
+constexpr int kFillBatch = 8;           // staged pieces loaded per thread before they are stored
 
+// Two consecutive lines (a 128-byte run of each row), loaded back to back so
+// that both halves of a row's 128-byte segment are requested together.
 template <int G>
-struct Line {
-  u4_t w[G];       // weight codes of each row group
-  uint32_t ws[G];  // their two E4M3 scale bytes
+struct Pair {
+  u4_t w[2][G];       // weight codes of each half and row group
+  uint32_t ws[2][G];  // their two E4M3 scale bytes
 };
 
-// LDS layout of the staged activations: 16 rows of codes, then 16
-// rows of scales, each row padded by 16 bytes so that the 16 rows read by one
-// quarter-wave fall in different banks.
-__host__ __device__ constexpr uint32_t alds_code_stride(int K) { return (uint32_t)K / 2 + 16u; }
-__host__ __device__ constexpr uint32_t alds_scale_stride(int K) { return (uint32_t)K / 16 + 16u; }
-__host__ __device__ constexpr uint32_t alds_bytes_m16(int K) { return 16u * (alds_code_stride(K) + alds_scale_stride(K)); }
+// LDS layout of the staged activations for LS lines: 16 rows of codes
+// (stride 64 LS + 16 bytes: 16-byte units per row step = 4 LS + 1, odd, so the
+// 16 rows read by a quarter-wave fall in distinct banks), then 16 rows of
+// scales (stride 8 LS + 4 bytes: an odd number of words).
+__host__ __device__ constexpr uint32_t cstride(int LS) { return 64u * (uint32_t)LS + 16u; }
+__host__ __device__ constexpr uint32_t sstride(int LS) { return 8u * (uint32_t)LS + 4u; }
+__host__ __device__ constexpr uint32_t alds_bytes(int LS) { return 16u * (cstride(LS) + sstride(LS)); }
 
-template <int G, bool OUT_BF16>
-__global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int LW) {
-  // LDS: the staged activation codes and scales, then the partial sums
-  // [waves][G][8 rows][16 activation rows].
+struct Plan {
+  int G;   // 16-row groups per wave
+  int RB;  // row blocks (waves with distinct rows) per workgroup
+  int KS;  // K slices per workgroup (waves splitting its lines)
+  int KZ;  // K splits over workgroups (grid.y); > 1 needs the workspace
+  int LS;  // lines per K split (the last split may have fewer)
+  int D;   // pairs of lines of weight loads in flight per wave
+  int CP;  // cache policy of the weight loads (2: non-temporal)
+};
+
+struct Split {
+  float* part;    // [KZ][M][N] fp32 partial sums (KZ > 1)
+  uint32_t* cnt;  // [row blocks] arrival counters, zero between calls
+};
+
+template <int G, int D, int CP, bool OUT_BF16>
+__global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int LS, Split sp) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_m16[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
+  const int RB = nw / KS;
   const int rb = wave / KS, kc = wave - rb * KS;
   const int M = p.M, K = p.K, N = p.N;
+  const int KZ = gridDim.y, kz = blockIdx.y;
   const uint32_t row_bytes = (uint32_t)K >> 1, srow = (uint32_t)K >> 4;
-  const int L = K >> 8;
-  const uint32_t row0 = (uint32_t)(blockIdx.x * (nw / KS) + rb) * 8u * G;
-  const int t0 = kc * LW;
-  const int t1 = t0 + LW < L ? t0 + LW : L;
+  const int L = K / kLine;
+  // the workgroup's lines [l0, l0 + Lr)
+  const int l0 = kz * LS;
+  const int Lr = (L - l0 < LS) ? L - l0 : LS;
+  // this wave's pairs of lines [u0, u1): lines [2 u0, t1)
+  const int Pr = (Lr + 1) >> 1;
+  const int PW = (Pr + KS - 1) / KS;
+  const int u0 = kc * PW < Pr ? kc * PW : Pr;
+  const int u1 = u0 + PW < Pr ? u0 + PW : Pr;
+  const int t1 = 2 * u1 < Lr ? 2 * u1 : Lr;
+  const uint32_t row0 = ((uint32_t)blockIdx.x * RB + rb) * 16u * G;
 
   const __amdgpu_buffer_rsrc_t ac = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.ac), (short)0, (int)((uint32_t)M * row_bytes), 0x00020000);
@@ -72,165 +108,235 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
   const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.ws), (short)0, (int)((uint32_t)N * srow), 0x00020000);
 
-  float* part = reinterpret_cast<float*>(lds_m16 + alds_bytes_m16(K));
   const int j = lane & 15, q = lane >> 4;
-  // Staged activations: 16-byte pieces, codes of rows 0..15 then their
-  // scales (rows past M as zeros).  All pieces of a thread are loaded before
-  // any is stored, and the first weight lines are requested in between.
-  const uint32_t cs = alds_code_stride(K), ss = alds_scale_stride(K);
-  const uint32_t cpr = row_bytes / 16u, spr = srow / 16u;  // pieces per row
-  const uint32_t cpieces = 16u * cpr, pieces = cpieces + 16u * spr;
-  u4_t fv[kFillMax];
-  {
-#pragma unroll
-    for (int s = 0; s < kFillMax; ++s) {
-      const uint32_t pc = threadIdx.x + blockDim.x * s;
-      const bool code = pc < cpieces;
-      const uint32_t pp = code ? pc : pc - cpieces;
-      const uint32_t r = code ? pp / cpr : pp / spr;
-      const uint32_t c = code ? pp - r * cpr : pp - r * spr;
-      const bool ok = pc < pieces && r < (uint32_t)M;
-      fv[s] = code ? __builtin_amdgcn_raw_buffer_load_b128(ac, ok ? r * row_bytes + 16u * c : kOOB, 0, 0)
-                   : __builtin_amdgcn_raw_buffer_load_b128(as, ok ? r * srow + 16u * c : kOOB, 0, 0);
-    }
-  }
-  auto fill_store = [&]() {
-    {
-#pragma unroll
-      for (int s = 0; s < kFillMax; ++s) {
-        const uint32_t pc = threadIdx.x + blockDim.x * s;
-        if (pc < pieces) {
-          const bool code = pc < cpieces;
-          const uint32_t pp = code ? pc : pc - cpieces;
-          const uint32_t r = code ? pp / cpr : pp / spr;
-          const uint32_t c = code ? pp - r * cpr : pp - r * spr;
-          *reinterpret_cast<u4_t*>(lds_m16 + (code ? r * cs : 16u * cs + r * ss) + 16u * c) = fv[s];
-        }
-      }
-      __syncthreads();
-    }
-  };
+  // weight row row0 + j (+ 16g): 16 code bytes at 64 t + 16 q, scale bytes 2q, 2q+1 of line t
+  const uint32_t w_off = (row0 + (uint32_t)j) * row_bytes + 16u * (uint32_t)q;
+  const uint32_t ws_off = (row0 + (uint32_t)j) * srow + 2u * (uint32_t)q;
 
-  // weight row row0 + j/2 (+ 8g), half j%2, elements 32q .. 32q+31 of the half
-  const uint32_t w_off = (row0 + (j >> 1)) * row_bytes + 64u * (j & 1) + 16u * q;
-  const uint32_t ws_off = (row0 + (j >> 1)) * srow + 8u * (j & 1) + 2u * q;
-
-  auto load = [&](int t) {
-    Line<G> d;
-    const bool ok = t < t1;
+  // pair u: lines 2u and 2u + 1 relative to l0 (l0 is even)
+  auto load = [&](int u) {
+    Pair<G> d;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      d.w[g] = __builtin_amdgcn_raw_buffer_load_b128(wc, ok ? w_off + 8u * g * row_bytes + 128u * t : kOOB, 0, 2);
-      d.ws[g] = __builtin_amdgcn_raw_buffer_load_b16(ws, ok ? ws_off + 8u * g * srow + 16u * t : kOOB, 0, 2);
+    for (int h = 0; h < 2; ++h) {
+      const int t = 2 * u + h;
+      const bool ok = t < t1;
+      const uint32_t tl = (uint32_t)(l0 + t);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        d.w[h][g] = __builtin_amdgcn_raw_buffer_load_b128(wc, ok ? w_off + 16u * g * row_bytes + 64u * tl : kOOB, 0, CP);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = 2 * u + h;
+      const bool ok = t < t1;
+      const uint32_t tl = (uint32_t)(l0 + t);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        d.ws[h][g] = __builtin_amdgcn_raw_buffer_load_b16(ws, ok ? ws_off + 16u * g * srow + 8u * tl : kOOB, 0, CP);
     }
     return d;
   };
+
+  Pair<G> buf[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    buf[d] = load(u0 + d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Stage the activations of lines [l0, l0 + Lr): 16-byte code pieces and
+  // 4-byte scale pieces, rows past M as zeros, a batch of loads per thread
+  // before its stores.
+  {
+    const uint32_t cs = cstride(LS), ss = sstride(LS);
+    const uint32_t cpr = 4u * (uint32_t)Lr, spr = 2u * (uint32_t)Lr;  // pieces per row
+    const uint32_t cpieces = 16u * cpr, spieces = 16u * spr;
+    for (uint32_t base = 0; base < cpieces; base += kFillBatch * blockDim.x) {
+      u4_t v[kFillBatch];
+#pragma unroll
+      for (int s = 0; s < kFillBatch; ++s) {
+        const uint32_t pc = base + threadIdx.x + blockDim.x * s;
+        const uint32_t r = pc / cpr, c = pc - r * cpr;
+        const bool ok = pc < cpieces && r < (uint32_t)M;
+        v[s] = __builtin_amdgcn_raw_buffer_load_b128(ac, ok ? r * row_bytes + 64u * l0 + 16u * c : kOOB, 0, 0);
+      }
+#pragma unroll
+      for (int s = 0; s < kFillBatch; ++s) {
+        const uint32_t pc = base + threadIdx.x + blockDim.x * s;
+        const uint32_t r = pc / cpr, c = pc - r * cpr;
+        if (pc < cpieces) *reinterpret_cast<u4_t*>(lds_m16 + r * cs + 16u * c) = v[s];
+      }
+    }
+    for (uint32_t base = 0; base < spieces; base += kFillBatch * blockDim.x) {
+      uint32_t v[kFillBatch];
+#pragma unroll
+      for (int s = 0; s < kFillBatch; ++s) {
+        const uint32_t pc = base + threadIdx.x + blockDim.x * s;
+        const uint32_t r = pc / spr, c = pc - r * spr;
+        const bool ok = pc < spieces && r < (uint32_t)M;
+        v[s] = __builtin_amdgcn_raw_buffer_load_b32(as, ok ? r * srow + 8u * l0 + 4u * c : kOOB, 0, 0);
+      }
+#pragma unroll
+      for (int s = 0; s < kFillBatch; ++s) {
+        const uint32_t pc = base + threadIdx.x + blockDim.x * s;
+        const uint32_t r = pc / spr, c = pc - r * spr;
+        if (pc < spieces) *reinterpret_cast<uint32_t*>(lds_m16 + 16u * cs + r * ss + 4u * c) = v[s];
+      }
+    }
+    __syncthreads();
+  }
 
   f4_t acc[G][2];
 #pragma unroll
   for (int g = 0; g < G; ++g) acc[g][0] = acc[g][1] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-  const uint8_t* a_lds = lds_m16 + (uint32_t)j * alds_code_stride(K) + 16u * q;
-  const uint8_t* as_lds = lds_m16 + 16u * alds_code_stride(K) + (uint32_t)j * alds_scale_stride(K) + 2u * q;
-  auto compute = [&](const Line<G>& d, int t) {
-    h8_t av[2][4];
+  // activation row j, elements 32q .. 32q+31 of each line
+  const uint8_t* a_lds = lds_m16 + (uint32_t)j * cstride(LS) + 16u * q;
+  const uint8_t* as_lds = lds_m16 + 16u * cstride(LS) + (uint32_t)j * sstride(LS) + 2u * q;
+  auto compute = [&](const Pair<G>& d, int u) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      // activation row j, elements 32q .. 32q+31 of half h of line t
-      const u4_t a = *reinterpret_cast<const u4_t*>(a_lds + 64u * h + 128u * t);
-      const uint32_t sa = *reinterpret_cast<const uint16_t*>(as_lds + 8u * h + 16u * t);
-      const h2_t s2 = e4m3x2_to_h2(sa);  // blocks 2q and 2q+1 of the half
+      const int t = 2 * u + h;
+      if (h == 1 && t >= t1) break;  // odd line count: no second half
+      const u4_t a = *reinterpret_cast<const u4_t*>(a_lds + 64u * t);
+      const h2_t sa = e4m3x2_to_h2(*reinterpret_cast<const uint16_t*>(as_lds + 8u * t));
+      h8_t av[4];
 #pragma unroll
-      for (int pc = 0; pc < 4; ++pc) av[h][pc] = dequant8(a[pc], pc < 2 ? s2.x : s2.y);
-    }
+      for (int pc = 0; pc < 4; ++pc) av[pc] = dequant8(a[pc], pc < 2 ? sa.x : sa.y);
+      h2_t sw[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const h2_t s2 = e4m3x2_to_h2(d.ws[g]);
+      for (int g = 0; g < G; ++g) sw[g] = e4m3x2_to_h2(d.ws[h][g]);
 #pragma unroll
       for (int pc = 0; pc < 4; ++pc) {
-        const h8_t wv = dequant8(d.w[g][pc], pc < 2 ? s2.x : s2.y);
-        acc[g][0] = mfma16x16x32(av[0][pc], wv, acc[g][0]);
-        acc[g][1] = mfma16x16x32(av[1][pc], wv, acc[g][1]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const h8_t wv = dequant8(d.w[h][g][pc], pc < 2 ? sw[g].x : sw[g].y);
+          acc[g][pc & 1] = mfma16x16x32(av[pc], wv, acc[g][pc & 1]);
+        }
       }
     }
   };
 
-  Line<G> b0 = load(t0);
-  __builtin_amdgcn_sched_barrier(0);
-  Line<G> b1 = load(t0 + 1);
-  __builtin_amdgcn_sched_barrier(0);
-  Line<G> b2 = load(t0 + 2);
-  __builtin_amdgcn_sched_barrier(0);
-  fill_store();
-  for (int t = t0; t < t1; t += 3) {
-    compute(b0, t);
-    __builtin_amdgcn_sched_barrier(0);
-    b0 = load(t + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    if (t + 1 < t1) compute(b1, t + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    b1 = load(t + 4);
-    __builtin_amdgcn_sched_barrier(0);
-    if (t + 2 < t1) compute(b2, t + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    b2 = load(t + 5);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int u = u0; u < u1; u += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (u + d < u1) compute(buf[d], u + d);
+      __builtin_amdgcn_sched_barrier(0);
+      buf[d] = load(u + d + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
-  // D[i][j] of half h sits in lane j + 16(i/4), element i%4: keep the half of
-  // this lane's column, add the two halves of a row, park [g][row][i] in LDS.
+  // D[i][j] sits in lane j + 16(i/4), element i%4: activation row m = 4q + e,
+  // weight row n = row0 + 16g + j.
+  f4_t v[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) v[g] = acc[g][0] + acc[g][1];
+
+  if (KS > 1) {  // add the K slices of the workgroup in order kc = 0, 1, ...
+    __syncthreads();  // the staged activations are dead; reuse the LDS
+    f4_t* part = reinterpret_cast<f4_t*>(lds_m16);
+    if (kc != 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) part[(wave * G + g) * 64 + lane] = v[g];
+    }
+    __syncthreads();
+    if (kc == 0) {
+      for (int k2 = 1; k2 < KS; ++k2) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) v[g] += part[((wave + k2) * G + g) * 64 + lane];
+      }
+    }
+  }
+
+  if (KZ > 1) {  // add the KZ partial tiles of this row block in order kz = 0, 1, ...
+    // The partials are written and read with device-scope (write-through,
+    // coherent across the XCDs' L2s) stores and loads; each thread waits for
+    // its stores to complete before the barrier after which one thread takes
+    // the ticket, so no L2-wide write-back or invalidation is needed.
+    __shared__ uint32_t ticket;
+    if (kc == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint32_t n = row0 + 16u * g + j;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 4 * q + e;
+          if (n < (uint32_t)N && m < M)
+            __hip_atomic_store(sp.part + ((int64_t)kz * M + m) * N + n, v[g][e], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0)
+      ticket = __hip_atomic_fetch_add(sp.cnt + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (ticket != (uint32_t)(KZ - 1)) return;
+    if (kc == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint32_t n = row0 + 16u * g + j;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 4 * q + e;
+          float s = 0.f;
+          if (n < (uint32_t)N && m < M) {
+            const float* pp = sp.part + (int64_t)m * N + n;
+            for (int z = 0; z < KZ; ++z)
+              s += __hip_atomic_load(pp + (int64_t)z * M * N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          v[g][e] = s;
+        }
+      }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(sp.cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (kc != 0) return;
+
+  const float gscale = (*p.ga) * (*p.gw);
+  uint64_t best[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const bool odd = (j & 1) != 0;
-    f4_t v;
-    v.x = odd ? acc[g][1].x : acc[g][0].x;
-    v.y = odd ? acc[g][1].y : acc[g][0].y;
-    v.z = odd ? acc[g][1].z : acc[g][0].z;
-    v.w = odd ? acc[g][1].w : acc[g][0].w;
-    v.x += __shfl_xor(v.x, 1);
-    v.y += __shfl_xor(v.y, 1);
-    v.z += __shfl_xor(v.z, 1);
-    v.w += __shfl_xor(v.w, 1);
-    if ((j & 1) == 0) *reinterpret_cast<f4_t*>(part + ((wave * G + g) * 8 + (j >> 1)) * 16 + 4 * q) = v;
-  }
-  __syncthreads();
-  if (kc != 0) return;
-  const float gscale = (*p.ga) * (*p.gw);
-  // With argmax keys, each lane keeps the best (value, column) of its
-  // activation row m = lane % 16 (idx steps by 64, so m is fixed per lane).
-  uint64_t best = 0;
-  for (int idx = lane; idx < G * 128; idx += 64) {
-    const int g = idx >> 7, r = (idx >> 4) & 7, m = idx & 15;
-    float s = 0.f;
-    for (int k2 = 0; k2 < KS; ++k2) s += part[(((rb * KS + k2) * G + g) * 8 + r) * 16 + m];
-    const uint32_t n = row0 + 8u * g + r;
-    if (n < (uint32_t)N && m < M) {
-      const float v = s * gscale;
-      if (p.argmax_keys) {
-        const uint64_t key = argmax_key(v, n);
-        best = key > best ? key : best;
-      }
-      if (p.out) {
-        const int64_t o = (int64_t)m * N + n;
-        if constexpr (OUT_BF16) {
-          reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(v);
-        } else {
-          reinterpret_cast<float*>(p.out)[o] = v;
+    const uint32_t n = row0 + 16u * g + j;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * q + e;
+      if (n < (uint32_t)N && m < M) {
+        const float val = v[g][e] * gscale;
+        if (p.argmax_keys) {
+          const uint64_t key = argmax_key(val, n);
+          best[e] = key > best[e] ? key : best[e];
+        }
+        if (p.out) {
+          const int64_t o = (int64_t)m * N + n;
+          if constexpr (OUT_BF16) {
+            reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(val);
+          } else {
+            reinterpret_cast<float*>(p.out)[o] = val;
+          }
         }
       }
     }
   }
   if (p.argmax_keys) {
-    // lanes m, m + 16, m + 32, m + 48 share row m; the maximum key is
-    // independent of the order in which the workgroups merge theirs.
-    uint64_t o = __shfl_xor(best, 16);
-    best = o > best ? o : best;
-    o = __shfl_xor(best, 32);
-    best = o > best ? o : best;
-    // spread over kKeySlots slots per row to keep same-address atomics few
+    // the 16 lanes of a quarter share rows 4q .. 4q+3; the maximum key does
+    // not depend on the order in which workgroups merge theirs.  Keys are
+    // spread over kKeySlots slots per row to keep same-address atomics few.
     const uint32_t slot = blockIdx.x % kKeySlots;
-    if (lane < M && best != 0)
-      atomicMax(reinterpret_cast<unsigned long long*>(p.argmax_keys) + slot * 16u + lane, best);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint64_t b = best[e];
+#pragma unroll
+      for (int x = 1; x < 16; x <<= 1) {
+        const uint64_t o = __shfl_xor(b, x);
+        b = o > b ? o : b;
+      }
+      const int m = 4 * q + e;
+      if (j == 0 && m < M && b != 0)
+        atomicMax(reinterpret_cast<unsigned long long*>(p.argmax_keys) + slot * 16u + m, b);
+    }
   }
 }
 
@@ -251,45 +357,116 @@ int device_cus() {
   return cus[dev];
 }
 
-template <int G>
-hipError_t launch_g(const GemmArgs& a, hipStream_t stream) {
-  const int L = a.K / 256;
-  const int64_t blocks = (a.N + 8 * G - 1) / (8 * G);  // row blocks of 8G rows
-  const int cus = device_cus();
-  // Split K over the waves of a workgroup until there are >= 8 waves per CU.
-  int KS = 1;
-  while (KS < 8 && KS < L && blocks * KS < 8LL * cus) ++KS;
+// Lines whose staged activations fit the LDS budget.
+constexpr int kMaxLS = 56;
+static_assert(alds_bytes(kMaxLS) <= (uint32_t)kMaxLdsM16, "staged activations exceed the LDS budget");
+
+// Launch plan, from a sweep over G x RB x KS x KZ x D on MI355X at the LM
+// head (16 x 5120 x 151936) and the tree-verification down-projection (16 x
+// 25600 x 5120): one 16-row group per wave (dequantizing the activation line
+// per wave costs less than the occupancy larger groups lose), eight waves with
+// distinct rows per workgroup, two pairs of lines in flight, cached loads.  K
+// is split over workgroups when the rows alone give fewer than ~4 waves per
+// CU (about 34 lines, 4352 K-elements, per split measured best) or when the
+// staged activations would not fit the LDS.  NVFP4_M16_{G,RB,KS,KZ,D,CP}
+// override the choice (tuning knobs; results change only by fp32 summation
+// order).
+constexpr int kSplitLines = 34;
+
+Plan make_plan(const GemmArgs& a, bool can_split) {
+  const int L = a.K / kLine;
+  const int64_t cus = device_cus();
+  Plan pl;
+  pl.G = 1;
+  const int e_g = env_int("NVFP4_M16_G", 0);
+  if (e_g == 1 || e_g == 2 || e_g == 4) pl.G = e_g;
+  pl.RB = 8;
+  const int e_rb = env_int("NVFP4_M16_RB", 0);
+  if (e_rb >= 1 && e_rb <= 8) pl.RB = e_rb;
+  pl.KS = 1;
   const int e_ks = env_int("NVFP4_M16_KS", 0);
-  if (e_ks > 0 && e_ks <= 8) KS = e_ks;
-  if (KS > L) KS = L;
-  const int LW = (L + KS - 1) / KS;
-  KS = (L + LW - 1) / LW;  // no wave without lines
-  const int nw = (KS >= 4 ? 1 : 4 / KS) * KS;  // row blocks x K slices: 3 to 8 waves
-  const int RB = nw / KS;
-  const dim3 grid((unsigned)((blocks + RB - 1) / RB));
-  const size_t lds = alds_bytes_m16(a.K) + (size_t)nw * G * 128 * sizeof(float);
-  if (a.out_bf16) gemm_m16_kernel<G, true><<<grid, 64 * nw, lds, stream>>>(a, KS, LW);
-  else gemm_m16_kernel<G, false><<<grid, 64 * nw, lds, stream>>>(a, KS, LW);
+  if (e_ks >= 1 && e_ks <= 8 && e_ks * pl.RB <= 8) pl.KS = e_ks;
+  const int64_t waves_per_split = ((a.N + 16 * pl.G - 1) / (16 * pl.G)) * pl.KS;
+  int KZ = 1;
+  if (can_split) {
+    if (waves_per_split < 4 * cus) KZ = (L + kSplitLines - 1) / kSplitLines;
+    const int e_kz = env_int("NVFP4_M16_KZ", 0);
+    if (e_kz >= 1) KZ = e_kz < L ? e_kz : L;
+  }
+  while ((L + KZ - 1) / KZ > kMaxLS) ++KZ;
+  pl.LS = (L + KZ - 1) / KZ;
+  pl.LS += pl.LS & (L > pl.LS ? 1 : 0);  // splits start on an even line (whole 128-byte runs)
+  pl.KZ = (L + pl.LS - 1) / pl.LS;       // no split without lines
+  pl.D = env_int("NVFP4_M16_D", 2);
+  if (pl.D != 1 && pl.D != 2 && pl.D != 4 && pl.D != 6) pl.D = 2;
+  pl.CP = env_int("NVFP4_M16_CP", 0) == 2 ? 2 : 0;
+  return pl;
+}
+
+int64_t row_blocks(const GemmArgs& a, const Plan& pl) {
+  return (a.N + 16 * pl.G * pl.RB - 1) / (16 * pl.G * pl.RB);
+}
+
+// Workspace layout: arrival counters (one per row block, rounded up to 256
+// bytes), then the fp32 partial sums [KZ][M][N].
+int64_t split_bytes(const GemmArgs& a, const Plan& pl) {
+  if (pl.KZ <= 1) return 0;
+  const int64_t cnt = (row_blocks(a, pl) * 4 + 255) / 256 * 256;
+  return cnt + (int64_t)pl.KZ * a.M * a.N * 4;
+}
+
+template <int G, int D, int CP>
+hipError_t launch_gd(const GemmArgs& a, const Plan& pl, Split sp, hipStream_t stream) {
+  const dim3 grid((unsigned)row_blocks(a, pl), (unsigned)pl.KZ);
+  const int nw = pl.RB * pl.KS;
+  uint32_t lds = alds_bytes(pl.LS);
+  const uint32_t part = (uint32_t)nw * G * 64 * 16;
+  if (pl.KS > 1 && part > lds) lds = part;
+  if (a.out_bf16) gemm_m16_kernel<G, D, CP, true><<<grid, 64 * nw, lds, stream>>>(a, pl.KS, pl.LS, sp);
+  else gemm_m16_kernel<G, D, CP, false><<<grid, 64 * nw, lds, stream>>>(a, pl.KS, pl.LS, sp);
   return hipGetLastError();
 }
 
-}  // namespace
-
-// The staged activations and the partial sums of up to 8 waves x 4 groups fit
-// in 64 KiB of LDS, and 3 waves' threads cover the staging pieces.
-bool gemm_m16_supported(const GemmArgs& a) {
-  return a.M >= 1 && a.M <= 16 && a.K % 256 == 0 && alds_bytes_m16(a.K) + 8u * 4u * 128u * 4u <= 64u * 1024u &&
-         16 * (a.K / 32 + a.K / 256) <= kFillMax * 64 * 3;
+template <int G>
+hipError_t launch_g(const GemmArgs& a, const Plan& pl, Split sp, hipStream_t stream) {
+  if (pl.CP == 2) return launch_gd<G, 2, 2>(a, pl, sp, stream);
+  switch (pl.D) {
+    case 1: return launch_gd<G, 1, 0>(a, pl, sp, stream);
+    case 4: return launch_gd<G, 4, 0>(a, pl, sp, stream);
+    case 6: return launch_gd<G, 6, 0>(a, pl, sp, stream);
+    default: return launch_gd<G, 2, 0>(a, pl, sp, stream);
+  }
 }
 
-// G (row groups sharing one dequantized activation operand): 4 when there are
-// enough rows for >= 4 row blocks per CU, else 2, else 1.
+bool have_workspace(const GemmArgs& a) { return a.workspace != nullptr && a.workspace_bytes > 0; }
+
+}  // namespace
+
+int64_t gemm_m16_workspace_bytes(const GemmArgs& a) {
+  if (a.M < 1 || a.M > 16 || a.K % kLine != 0 || a.N < 1) return 0;
+  return split_bytes(a, make_plan(a, true));
+}
+
+// Any K that is a multiple of 128: with a large enough workspace the lines
+// are split over workgroups as needed; without one, the staged activations of
+// the whole K must fit the LDS (K <= 7168).
+bool gemm_m16_supported(const GemmArgs& a) {
+  if (a.M < 1 || a.M > 16 || a.K % kLine != 0) return false;
+  const bool split = have_workspace(a) && a.workspace_bytes >= gemm_m16_workspace_bytes(a);
+  return split || a.K / kLine <= kMaxLS;
+}
+
 hipError_t launch_gemm_m16(const GemmArgs& a, hipStream_t stream) {
-  const int64_t cus = device_cus();
-  int G = a.N >= 32 * 4 * cus ? 4 : a.N >= 16 * cus ? 2 : 1;
-  const int e_g = env_int("NVFP4_M16_G", 0);
-  if (e_g == 1 || e_g == 2 || e_g == 4) G = e_g;
-  return G == 4 ? launch_g<4>(a, stream) : G == 2 ? launch_g<2>(a, stream) : launch_g<1>(a, stream);
+  const bool split = have_workspace(a) && a.workspace_bytes >= gemm_m16_workspace_bytes(a);
+  const Plan pl = make_plan(a, split);
+  Split sp{nullptr, nullptr};
+  if (pl.KZ > 1) {
+    const int64_t cnt = (row_blocks(a, pl) * 4 + 255) / 256 * 256;
+    sp.cnt = reinterpret_cast<uint32_t*>(a.workspace);
+    sp.part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.workspace) + cnt);
+  }
+  return pl.G == 4 ? launch_g<4>(a, pl, sp, stream) : pl.G == 2 ? launch_g<2>(a, pl, sp, stream)
+                                                              : launch_g<1>(a, pl, sp, stream);
 }
 
 }  // namespace nvfp4

@@ -40,6 +40,12 @@ struct GemmArgs {
   // argmax_key() into argmax_keys[slot][m], slot = workgroup % kKeySlots
   // ([kKeySlots][16] words, zero on entry); out may then be NULL.
   uint64_t* argmax_keys = nullptr;
+  // Caller-owned device workspace (gemm_m16 only): when at least
+  // gemm_m16_workspace_bytes() large, long K is split over workgroups.  Its
+  // first bytes are arrival counters that must be zero on entry and are zero
+  // again when the kernel ends.
+  void* workspace = nullptr;
+  int64_t workspace_bytes = 0;
 };
 
 constexpr int kKeySlots = 64;  // argmax key slots per row
@@ -64,8 +70,11 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
 bool gemv_fp4_supported(const GemmArgs& a);
 hipError_t launch_gemv_fp4(const GemmArgs& a, hipStream_t stream);
 
-// Weight-streaming GEMM for M <= 16 on f16 matrix cores (K % 256 == 0).
+// Weight-streaming GEMM for M <= 16 on f16 matrix cores (K % 128 == 0; without
+// a workspace K <= 7168).  gemm_m16_workspace_bytes() is the workspace that
+// lets it split K over workgroups (0 when it would not).
 bool gemm_m16_supported(const GemmArgs& a);
+int64_t gemm_m16_workspace_bytes(const GemmArgs& a);
 hipError_t launch_gemm_m16(const GemmArgs& a, hipStream_t stream);
 
 // LDS-tiled MFMA path for large M.

@@ -42,7 +42,7 @@ def test_status_strings_and_version(lib):
     for s in range(6):
         assert B.status_string(s)
     assert B.status_string(99) == "unknown status"
-    assert lib.nvfp4_abi_version() == 5
+    assert lib.nvfp4_abi_version() == 6
 
 
 def gemm(lib, M, K, N, ptrs=(A16,) * 7, out_dt=B.NVFP4_BF16, path=B.PATH_AUTO):
@@ -73,6 +73,20 @@ def test_gemm_rejects_null_align_dtype_path(lib):
     assert gemm(lib, 1, 32, 16, ptrs=(A16,) * 2 + (A16 + 4,) + (A16,) * 4, out_dt=7) == B.NVFP4_ERR_DTYPE
     assert gemm(lib, 1, 32, 16, path=3) == B.NVFP4_ERR_DTYPE
     assert lib.nvfp4_gemm(1, 32, 16, A16, A16, A16, A16, A16, A16, A16, 2, None) == B.NVFP4_ERR_DTYPE
+
+
+def test_gemm_ws_validation(lib):
+    """nvfp4_gemm_ws validates like nvfp4_gemm, plus its workspace (size, NULL, alignment)."""
+    def ws(M, K, N, work=A16, nbytes=4096, out_dt=B.NVFP4_BF16, ptrs=(A16,) * 7):
+        ac, asc, ga, wc, wsc, gw, out = ptrs
+        return lib.nvfp4_gemm_ws(M, K, N, ac, asc, ga, wc, wsc, gw, out, out_dt, work, nbytes, None)
+    assert ws(16, 256, 64, out_dt=3) == B.NVFP4_ERR_DTYPE
+    assert ws(16, 24, 64) == B.NVFP4_ERR_SHAPE
+    assert ws(16, 256, 64, nbytes=-1) == B.NVFP4_ERR_SHAPE
+    assert ws(16, 256, 64, work=0) == B.NVFP4_ERR_NULL
+    assert ws(16, 256, 64, work=A16 + 8) == B.NVFP4_ERR_ALIGN
+    assert ws(16, 256, 64, ptrs=(A16,) * 6 + (0,)) == B.NVFP4_ERR_NULL
+    assert ws(0, 256, 64, work=0, nbytes=0, ptrs=(0,) * 7) == B.NVFP4_OK
 
 
 def test_empty_gemm_is_ok_without_pointers(lib):

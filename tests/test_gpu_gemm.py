@@ -149,7 +149,7 @@ def test_gemm_empty():
 # Full-size workloads, auto path (the launch configuration the benchmark times).
 # ---------------------------------------------------------------------------
 
-def _full(name, n_sample=384):
+def _full(name, n_sample=384, workspace="auto"):
     wl = WL.get(name)
     inp = WL.generate(wl)
     a = inp.a_f32()
@@ -157,7 +157,7 @@ def _full(name, n_sample=384):
     wc, ws, gw = B.nvfp4_quantize_weights(U.dev_f32(inp.W))
     ac, asc = B.nvfp4_quantize_act(U.dev_acts(inp), U.scalar(g_a))
     out_dtype = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
-    out = U.host(B.nvfp4_gemm(ac, asc, U.scalar(g_a), wc, ws, gw, out_dtype=out_dtype))
+    out = U.host(B.nvfp4_gemm(ac, asc, U.scalar(g_a), wc, ws, gw, out_dtype=out_dtype, workspace=workspace))
     rng = np.random.default_rng(3)
     cols = np.unique(np.concatenate([[0, wl.N - 1], rng.choice(wl.N, min(n_sample, wl.N), replace=False)]))
     g_w = Q.global_scale(inp.W)
@@ -167,9 +167,12 @@ def _full(name, n_sample=384):
     return wl, out, cols, C, T
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode_up", "verify_down", "lm_head"])
-def test_full_size_sampled_outputs(name):
-    wl, out, cols, C, T = _full(name)
+@pytest.mark.parametrize("name,workspace", [("tiny", "auto"), ("decode_up", "auto"), ("verify_down", "auto"),
+                                            ("verify_down", None), ("lm_head", "auto")])
+def test_full_size_sampled_outputs(name, workspace):
+    """Sampled outputs at full size, in the benchmark's launch configuration (the automatic path
+    with the cached workspace), and the tree-verification down-projection without one."""
+    wl, out, cols, C, T = _full(name, workspace=workspace)
     # precondition for the strict bound with a bf16 result: the output rounding (2^-8 |C|)
     # must fit inside 1e-3 * sum|a*w|
     if wl.out_dtype == "bf16":
