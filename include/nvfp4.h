@@ -246,7 +246,7 @@ nvfp4_status nvfp4_tree_accept(int64_t n_nodes, const int32_t* parent, const int
  *            nodes' NVFP4 activations a_* and the LM-head weights w_*.
  *   parent, draft: as nvfp4_tree_accept.
  *   logits   optional out [M][N] fp32 (may be NULL when K % 128 == 0 and
- *            K <= 7168: the argmax is then fused into the GEMM and the logits
+ *            K <= 6272: the argmax is then fused into the GEMM and the logits
  *            are not written; other K need it).
  *   greedy   out [M] int32: each row's argmax (lowest column on ties; -0.0
  *            orders just below +0.0).

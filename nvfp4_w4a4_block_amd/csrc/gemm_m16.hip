@@ -49,9 +49,19 @@ constexpr int kFillBatch = 8;           // staged pieces loaded per thread befor
 // that both halves of a row's 128-byte segment are requested together.
 template <int G>
 struct Pair {
-  u4_t w[2][G];       // weight codes of each half and row group
-  uint32_t ws[2][G];  // their two E4M3 scale bytes
+  u4_t w[2][G];  // weight codes of each half and row group
 };
+
+// Weight scales are fetched a block of 8 lines (4 pairs) at a time: lane
+// j + 16c loads 16 bytes of row j (lines 2c and 2c + 1 of the block), so one
+// load covers 16 rows x 64 contiguous bytes, and the block is parked in a
+// per-wave LDS slot of 16 rows x 64 bytes whose dwords are XOR-swizzled by
+// row (dword d of row j at 4 (d ^ j)), so the 2-byte reads of a quarter-wave
+// (16 rows, one offset) hit distinct banks.  Per-lane 2-byte scale loads from
+// memory touch 16 cache lines for 128 bytes and cost as much time as the
+// codes (measured: the code stream alone runs at 5.5 TB/s, with such scale
+// loads at 3.6 TB/s).
+constexpr uint32_t kScaleSlot = 16u * 64u;  // LDS bytes per wave and row group
 
 // LDS layout of the staged activations for LS lines: 16 rows of codes
 // (stride 64 LS + 16 bytes: 16-byte units per row step = 4 LS + 1, odd, so the
@@ -60,6 +70,10 @@ struct Pair {
 __host__ __device__ constexpr uint32_t cstride(int LS) { return 64u * (uint32_t)LS + 16u; }
 __host__ __device__ constexpr uint32_t sstride(int LS) { return 8u * (uint32_t)LS + 4u; }
 __host__ __device__ constexpr uint32_t alds_bytes(int LS) { return 16u * (cstride(LS) + sstride(LS)); }
+// LDS of a workgroup: the staged activations, then one scale slot per wave and row group.
+__host__ __device__ constexpr uint32_t lds_bytes(int LS, int waves, int G) {
+  return alds_bytes(LS) + (uint32_t)waves * (uint32_t)G * kScaleSlot;
+}
 
 struct Plan {
   int G;   // 16-row groups per wave
@@ -109,9 +123,8 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
       const_cast<uint8_t*>(p.ws), (short)0, (int)((uint32_t)N * srow), 0x00020000);
 
   const int j = lane & 15, q = lane >> 4;
-  // weight row row0 + j (+ 16g): 16 code bytes at 64 t + 16 q, scale bytes 2q, 2q+1 of line t
+  // weight row row0 + j (+ 16g): 16 code bytes at 64 t + 16 q of line t
   const uint32_t w_off = (row0 + (uint32_t)j) * row_bytes + 16u * (uint32_t)q;
-  const uint32_t ws_off = (row0 + (uint32_t)j) * srow + 2u * (uint32_t)q;
 
   // pair u: lines 2u and 2u + 1 relative to l0 (l0 is even)
   auto load = [&](int u) {
@@ -125,18 +138,32 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
       for (int g = 0; g < G; ++g)
         d.w[h][g] = __builtin_amdgcn_raw_buffer_load_b128(wc, ok ? w_off + 16u * g * row_bytes + 64u * tl : kOOB, 0, CP);
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = 2 * u + h;
-      const bool ok = t < t1;
-      const uint32_t tl = (uint32_t)(l0 + t);
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-        d.ws[h][g] = __builtin_amdgcn_raw_buffer_load_b16(ws, ok ? ws_off + 16u * g * srow + 8u * tl : kOOB, 0, CP);
-    }
     return d;
   };
+  // scale block starting at pair ub: lane j + 16c gets row j's scale bytes of
+  // lines 2ub + 2c and 2ub + 2c + 1
+  const uint32_t sb_off = (row0 + (uint32_t)j) * srow + 16u * (uint32_t)q;
+  auto load_scales = [&](int ub, u4_t (&sb)[G]) {
+    const int t = 2 * ub + 2 * q;
+    const bool ok = t < t1;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      sb[g] = __builtin_amdgcn_raw_buffer_load_b128(ws, ok ? sb_off + 16u * g * srow + 8u * (uint32_t)(l0 + 2 * ub) : kOOB, 0, CP);
+  };
+  uint8_t* const w_slot = lds_m16 + alds_bytes(LS) + (uint32_t)wave * G * kScaleSlot + 64u * (uint32_t)j;
+  auto park_scales = [&](const u4_t (&sb)[G]) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint32_t*>(w_slot + g * kScaleSlot + 4u * ((4u * q + i) ^ (uint32_t)j)) = sb[g][i];
+    }
+  };
 
+  u4_t sX[G], sY[G];
+  load_scales(u0, sX);
+  load_scales(u0 + 4, sY);
+  __builtin_amdgcn_sched_barrier(0);
   Pair<G> buf[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
@@ -184,6 +211,12 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
       }
     }
     __syncthreads();
+    // Every load issued so far has landed (the staging stores waited for
+    // them, and they are younger than the first weight loads).  Saying so
+    // explicitly lets the compiler's wait-count analysis start the main loop
+    // from an empty state; otherwise it cannot prove the staging loads done and
+    // drains the whole prefetch ring at the top of every iteration.
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
   f4_t acc[G][2];
@@ -193,7 +226,13 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
   // activation row j, elements 32q .. 32q+31 of each line
   const uint8_t* a_lds = lds_m16 + (uint32_t)j * cstride(LS) + 16u * q;
   const uint8_t* as_lds = lds_m16 + 16u * cstride(LS) + (uint32_t)j * sstride(LS) + 2u * q;
-  auto compute = [&](const Pair<G>& d, int u) {
+  // line r of the current scale block: this lane's two scale bytes 2q, 2q+1
+  auto w_scale = [&](int g, int r) {
+    const uint32_t dw = 2u * (uint32_t)r + ((uint32_t)q >> 1);
+    return (uint32_t)*reinterpret_cast<const uint16_t*>(w_slot + g * kScaleSlot + 4u * (dw ^ (uint32_t)j) +
+                                                        2u * ((uint32_t)q & 1u));
+  };
+  auto compute = [&](const Pair<G>& d, int u, int p) {  // p: pair within the scale block
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t = 2 * u + h;
@@ -205,7 +244,7 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
       for (int pc = 0; pc < 4; ++pc) av[pc] = dequant8(a[pc], pc < 2 ? sa.x : sa.y);
       h2_t sw[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) sw[g] = e4m3x2_to_h2(d.ws[h][g]);
+      for (int g = 0; g < G; ++g) sw[g] = e4m3x2_to_h2(w_scale(g, 2 * p + h));
 #pragma unroll
       for (int pc = 0; pc < 4; ++pc) {
 #pragma unroll
@@ -217,14 +256,24 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
     }
   };
 
-  for (int u = u0; u < u1; u += D) {
+  // One scale block = 4 pairs; D (1, 2 or 4) divides it, so ring slot p % D
+  // holds pair ub + p.  Two blocks per iteration alternate the scale
+  // registers: park block k, request block k + 2, compute block k.
+  auto block = [&](int ub, u4_t (&sb)[G]) {
+    park_scales(sb);
+    load_scales(ub + 8, sb);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      if (u + d < u1) compute(buf[d], u + d);
+    for (int p = 0; p < 4; ++p) {
+      if (ub + p < u1) compute(buf[p % D], ub + p, p);
       __builtin_amdgcn_sched_barrier(0);
-      buf[d] = load(u + d + D);
+      buf[p % D] = load(ub + p + D);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  for (int ub = u0; ub < u1; ub += 8) {
+    block(ub, sX);
+    if (ub + 4 < u1) block(ub + 4, sY);
   }
 
   // D[i][j] sits in lane j + 16(i/4), element i%4: activation row m = 4q + e,
@@ -275,21 +324,38 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
     __syncthreads();
     if (ticket != (uint32_t)(KZ - 1)) return;
     if (kc == 0) {
+      // Four splits' partials are requested at once (one round trip each
+      // four), then added in the order z = 0, 1, ...
+      f4_t tot[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const uint32_t n = row0 + 16u * g + j;
+      for (int g = 0; g < G; ++g) tot[g] = f4_t{0.f, 0.f, 0.f, 0.f};
+      for (int z0 = 0; z0 < KZ; z0 += 4) {
+        f4_t r[4][G];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = 4 * q + e;
-          float s = 0.f;
-          if (n < (uint32_t)N && m < M) {
-            const float* pp = sp.part + (int64_t)m * N + n;
-            for (int z = 0; z < KZ; ++z)
-              s += __hip_atomic_load(pp + (int64_t)z * M * N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int zz = 0; zz < 4; ++zz) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const uint32_t n = row0 + 16u * g + j;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int m = 4 * q + e;
+              r[zz][g][e] = (z0 + zz < KZ && n < (uint32_t)N && m < M)
+                                ? __hip_atomic_load(sp.part + ((int64_t)(z0 + zz) * M + m) * N + n, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT)
+                                : 0.f;
+            }
           }
-          v[g][e] = s;
+        }
+#pragma unroll
+        for (int zz = 0; zz < 4; ++zz) {
+          if (z0 + zz < KZ) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) tot[g] += r[zz][g];
+          }
         }
       }
+#pragma unroll
+      for (int g = 0; g < G; ++g) v[g] = tot[g];
     }
     if (threadIdx.x == 0) __hip_atomic_store(sp.cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -357,9 +423,12 @@ int device_cus() {
   return cus[dev];
 }
 
-// Lines whose staged activations fit the LDS budget.
-constexpr int kMaxLS = 56;
-static_assert(alds_bytes(kMaxLS) <= (uint32_t)kMaxLdsM16, "staged activations exceed the LDS budget");
+// The most lines whose staged activations fit the LDS budget next to the
+// scale slots of `slots` (waves x row groups): 49 for eight single-group waves.
+constexpr int max_ls(int slots) {
+  return (int)(((uint32_t)kMaxLdsM16 / 16u - 4u * kScaleSlot / 64u * (uint32_t)slots - 20u) / 72u);
+}
+static_assert(lds_bytes(max_ls(8), 8, 1) <= (uint32_t)kMaxLdsM16 && max_ls(32) >= 1, "LDS budget");
 
 // Launch plan, from a sweep over G x RB x KS x KZ x D on MI355X at the LM
 // head (16 x 5120 x 151936) and the tree-verification down-projection (16 x
@@ -393,12 +462,14 @@ Plan make_plan(const GemmArgs& a, bool can_split) {
     const int e_kz = env_int("NVFP4_M16_KZ", 0);
     if (e_kz >= 1) KZ = e_kz < L ? e_kz : L;
   }
-  while ((L + KZ - 1) / KZ > kMaxLS) ++KZ;
+  const int mls = max_ls(pl.RB * pl.KS * pl.G);
+  while ((L + KZ - 1) / KZ > mls) ++KZ;
   pl.LS = (L + KZ - 1) / KZ;
   pl.LS += pl.LS & (L > pl.LS ? 1 : 0);  // splits start on an even line (whole 128-byte runs)
   pl.KZ = (L + pl.LS - 1) / pl.LS;       // no split without lines
   pl.D = env_int("NVFP4_M16_D", 2);
-  if (pl.D != 1 && pl.D != 2 && pl.D != 4 && pl.D != 6) pl.D = 2;
+  if (pl.D != 1 && pl.D != 2 && pl.D != 4) pl.D = 2;
+  if (pl.G == 4 && pl.D == 4) pl.D = 2;  // would spill registers
   pl.CP = env_int("NVFP4_M16_CP", 0) == 2 ? 2 : 0;
   return pl;
 }
@@ -419,9 +490,7 @@ template <int G, int D, int CP>
 hipError_t launch_gd(const GemmArgs& a, const Plan& pl, Split sp, hipStream_t stream) {
   const dim3 grid((unsigned)row_blocks(a, pl), (unsigned)pl.KZ);
   const int nw = pl.RB * pl.KS;
-  uint32_t lds = alds_bytes(pl.LS);
-  const uint32_t part = (uint32_t)nw * G * 64 * 16;
-  if (pl.KS > 1 && part > lds) lds = part;
+  const uint32_t lds = lds_bytes(pl.LS, nw, G);  // >= the KS partial sums (nw * G KiB)
   if (a.out_bf16) gemm_m16_kernel<G, D, CP, true><<<grid, 64 * nw, lds, stream>>>(a, pl.KS, pl.LS, sp);
   else gemm_m16_kernel<G, D, CP, false><<<grid, 64 * nw, lds, stream>>>(a, pl.KS, pl.LS, sp);
   return hipGetLastError();
@@ -433,7 +502,6 @@ hipError_t launch_g(const GemmArgs& a, const Plan& pl, Split sp, hipStream_t str
   switch (pl.D) {
     case 1: return launch_gd<G, 1, 0>(a, pl, sp, stream);
     case 4: return launch_gd<G, 4, 0>(a, pl, sp, stream);
-    case 6: return launch_gd<G, 6, 0>(a, pl, sp, stream);
     default: return launch_gd<G, 2, 0>(a, pl, sp, stream);
   }
 }
@@ -449,16 +517,17 @@ int64_t gemm_m16_workspace_bytes(const GemmArgs& a) {
 
 // Any K that is a multiple of 128: with a large enough workspace the lines
 // are split over workgroups as needed; without one, the staged activations of
-// the whole K must fit the LDS (K <= 7168).
+// the whole K must fit the LDS (K <= 6272 with the default plan).
 bool gemm_m16_supported(const GemmArgs& a) {
   if (a.M < 1 || a.M > 16 || a.K % kLine != 0) return false;
   const bool split = have_workspace(a) && a.workspace_bytes >= gemm_m16_workspace_bytes(a);
-  return split || a.K / kLine <= kMaxLS;
+  return split || make_plan(a, false).KZ == 1;
 }
 
 hipError_t launch_gemm_m16(const GemmArgs& a, hipStream_t stream) {
   const bool split = have_workspace(a) && a.workspace_bytes >= gemm_m16_workspace_bytes(a);
   const Plan pl = make_plan(a, split);
+  if (pl.KZ > 1 && !split) return hipErrorInvalidValue;  // callers check gemm_m16_supported() first
   Split sp{nullptr, nullptr};
   if (pl.KZ > 1) {
     const int64_t cnt = (row_blocks(a, pl) * 4 + 255) / 256 * 256;
