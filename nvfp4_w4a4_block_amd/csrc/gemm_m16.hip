@@ -70,9 +70,31 @@ constexpr uint32_t kScaleSlot = 16u * 64u;  // LDS bytes per wave and row group
 __host__ __device__ constexpr uint32_t cstride(int LS) { return 64u * (uint32_t)LS + 16u; }
 __host__ __device__ constexpr uint32_t sstride(int LS) { return 8u * (uint32_t)LS + 4u; }
 __host__ __device__ constexpr uint32_t alds_bytes(int LS) { return 16u * (cstride(LS) + sstride(LS)); }
-// LDS of a workgroup: the staged activations, then one scale slot per wave and row group.
-__host__ __device__ constexpr uint32_t lds_bytes(int LS, int waves, int G) {
-  return alds_bytes(LS) + (uint32_t)waves * (uint32_t)G * kScaleSlot;
+// Shared activation window (AW mode): the workgroup dequantizes 4 lines of the
+// 16 activation rows at a time into f16 in LDS, double-buffered (row stride
+// 1040 bytes = 65 16-byte units, odd, so a quarter-wave's 16 rows hit
+// distinct banks), and every wave reads its A operand from there instead of
+// dequantizing it itself.
+constexpr int kWin = 4;                                  // lines per window
+constexpr uint32_t kWinRow = kWin * kLine * 2 + 16;      // bytes per row of a window
+constexpr uint32_t kWinSlot = 16u * kWinRow;             // one window
+constexpr int kAwThreads = 512;                          // AW workgroups: 8 waves, one 16-block each
+static_assert(16 * kWin * kLine / 16 == kAwThreads, "one 16-element block per thread and window");
+
+__host__ __device__ constexpr uint32_t a_region(bool aw, int LS) { return aw ? 2u * kWinSlot : alds_bytes(LS); }
+// LDS of a workgroup: the activations, then one scale slot per wave and row group.
+__host__ __device__ constexpr uint32_t lds_bytes(int LS, int waves, int G, bool aw = false) {
+  return a_region(aw, LS) + (uint32_t)waves * (uint32_t)G * kScaleSlot;
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are done,
+// vector-memory loads stay in flight, and the compiler moves no memory access
+// across it.
+__device__ __forceinline__ void barrier_lds() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 struct Plan {
@@ -83,6 +105,7 @@ struct Plan {
   int LS;  // lines per K split (the last split may have fewer)
   int D;   // pairs of lines of weight loads in flight per wave
   int CP;  // cache policy of the weight loads (2: non-temporal)
+  bool AW; // shared activation window (G = 1, RB = 8, KS = 1)
 };
 
 struct Split {
@@ -90,8 +113,8 @@ struct Split {
   uint32_t* cnt;  // [row blocks] arrival counters, zero between calls
 };
 
-template <int G, int D, int CP, bool OUT_BF16>
-__global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int LS, Split sp) {
+template <int G, int D, int CP, bool OUT_BF16, int MAXT = 512, bool AW = false>
+__global__ __launch_bounds__(MAXT) void gemm_m16_kernel(GemmArgs p, int KS, int LS, Split sp) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_m16[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -150,7 +173,7 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
     for (int g = 0; g < G; ++g)
       sb[g] = __builtin_amdgcn_raw_buffer_load_b128(ws, ok ? sb_off + 16u * g * srow + 8u * (uint32_t)(l0 + 2 * ub) : kOOB, 0, CP);
   };
-  uint8_t* const w_slot = lds_m16 + alds_bytes(LS) + (uint32_t)wave * G * kScaleSlot + 64u * (uint32_t)j;
+  uint8_t* const w_slot = lds_m16 + a_region(AW, LS) + (uint32_t)wave * G * kScaleSlot + 64u * (uint32_t)j;
   auto park_scales = [&](const u4_t (&sb)[G]) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -171,6 +194,30 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  // AW: thread i dequantizes 16-element block i of each window: row i / 32,
+  // block i % 32 (line (i % 32) / 8 of the window, block i % 8 of that line).
+  const uint32_t aw_r = threadIdx.x >> 5, aw_b = threadIdx.x & 31;
+  u2_t aw_c = {0u, 0u};
+  uint32_t aw_s = 0;
+  auto aw_load = [&](int w) {  // window w: lines 4w .. 4w+3 relative to l0
+    const int t = kWin * w + (int)(aw_b >> 3);
+    const bool ok = aw_r < (uint32_t)M && t < Lr;
+    const uint32_t k16 = 8u * (uint32_t)(l0 + kWin * w) + aw_b;  // 16-element block index in the row
+    aw_c = __builtin_amdgcn_raw_buffer_load_b64(ac, ok ? aw_r * row_bytes + 8u * k16 : kOOB, 0, 0);
+    aw_s = __builtin_amdgcn_raw_buffer_load_b8(as, ok ? aw_r * srow + k16 : kOOB, 0, 0);
+  };
+  auto aw_store = [&](int w) {
+    const _Float16 sc = (_Float16)e4m3_to_f32(aw_s);
+    uint8_t* dst = lds_m16 + (uint32_t)(w & 1) * kWinSlot + aw_r * kWinRow + 32u * aw_b;
+    *reinterpret_cast<h8_t*>(dst) = dequant8(aw_c.x, sc);
+    *reinterpret_cast<h8_t*>(dst + 16) = dequant8(aw_c.y, sc);
+  };
+  if constexpr (AW) {
+    aw_load(0);
+    aw_store(0);
+    aw_load(1);
+    barrier_lds();
+  } else {
   // Stage the activations of lines [l0, l0 + Lr): 16-byte code pieces and
   // 4-byte scale pieces, rows past M as zeros, a batch of loads per thread
   // before its stores.
@@ -219,13 +266,15 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
     __builtin_amdgcn_s_waitcnt(0);
   }
 
+  }
+
   f4_t acc[G][2];
 #pragma unroll
   for (int g = 0; g < G; ++g) acc[g][0] = acc[g][1] = f4_t{0.f, 0.f, 0.f, 0.f};
 
   // activation row j, elements 32q .. 32q+31 of each line
-  const uint8_t* a_lds = lds_m16 + (uint32_t)j * cstride(LS) + 16u * q;
-  const uint8_t* as_lds = lds_m16 + 16u * cstride(LS) + (uint32_t)j * sstride(LS) + 2u * q;
+  [[maybe_unused]] const uint8_t* a_lds = lds_m16 + (uint32_t)j * cstride(LS) + 16u * q;
+  [[maybe_unused]] const uint8_t* as_lds = lds_m16 + 16u * cstride(LS) + (uint32_t)j * sstride(LS) + 2u * q;
   // line r of the current scale block: this lane's two scale bytes 2q, 2q+1
   auto w_scale = [&](int g, int r) {
     const uint32_t dw = 2u * (uint32_t)r + ((uint32_t)q >> 1);
@@ -237,11 +286,18 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
     for (int h = 0; h < 2; ++h) {
       const int t = 2 * u + h;
       if (h == 1 && t >= t1) break;  // odd line count: no second half
-      const u4_t a = *reinterpret_cast<const u4_t*>(a_lds + 64u * t);
-      const h2_t sa = e4m3x2_to_h2(*reinterpret_cast<const uint16_t*>(as_lds + 8u * t));
       h8_t av[4];
+      if constexpr (AW) {
+        const uint8_t* src = lds_m16 + (uint32_t)((t / kWin) & 1) * kWinSlot + (uint32_t)j * kWinRow +
+                             2u * (uint32_t)(kLine * (t % kWin) + 32 * q);
 #pragma unroll
-      for (int pc = 0; pc < 4; ++pc) av[pc] = dequant8(a[pc], pc < 2 ? sa.x : sa.y);
+        for (int pc = 0; pc < 4; ++pc) av[pc] = *reinterpret_cast<const h8_t*>(src + 16 * pc);
+      } else {
+        const u4_t a = *reinterpret_cast<const u4_t*>(a_lds + 64u * t);
+        const h2_t sa = e4m3x2_to_h2(*reinterpret_cast<const uint16_t*>(as_lds + 8u * t));
+#pragma unroll
+        for (int pc = 0; pc < 4; ++pc) av[pc] = dequant8(a[pc], pc < 2 ? sa.x : sa.y);
+      }
       h2_t sw[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) sw[g] = e4m3x2_to_h2(w_scale(g, 2 * p + h));
@@ -265,10 +321,21 @@ __global__ __launch_bounds__(512) void gemm_m16_kernel(GemmArgs p, int KS, int L
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
+      if constexpr (AW) {
+        if ((p & 1) == 0) {  // window w = (ub + p) / 2 begins: store window w + 1, request w + 2
+          const int w = (ub + p) >> 1;
+          aw_store(w + 1);
+          aw_load(w + 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       if (ub + p < u1) compute(buf[p % D], ub + p, p);
       __builtin_amdgcn_sched_barrier(0);
       buf[p % D] = load(ub + p + D);
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (AW) {
+        if (p & 1) barrier_lds();  // window w done everywhere; window w + 1 stored everywhere
+      }
     }
   };
   for (int ub = u0; ub < u1; ub += 8) {
@@ -430,16 +497,16 @@ constexpr int max_ls(int slots) {
 }
 static_assert(lds_bytes(max_ls(8), 8, 1) <= (uint32_t)kMaxLdsM16 && max_ls(32) >= 1, "LDS budget");
 
-// Launch plan, from a sweep over G x RB x KS x KZ x D on MI355X at the LM
-// head (16 x 5120 x 151936) and the tree-verification down-projection (16 x
-// 25600 x 5120): one 16-row group per wave (dequantizing the activation line
-// per wave costs less than the occupancy larger groups lose), eight waves with
-// distinct rows per workgroup, two pairs of lines in flight, cached loads.  K
+// Launch plan, from a sweep over G x RB x KS x KZ x D x AW on MI355X at the
+// LM head (16 x 5120 x 151936) and the tree-verification down-projection (16 x
+// 25600 x 5120): one 16-row group per wave, eight waves with distinct rows per
+// workgroup sharing one dequantized activation window (AW), two pairs of lines
+// in flight, cached loads.  K
 // is split over workgroups when the rows alone give fewer than ~4 waves per
 // CU (about 34 lines, 4352 K-elements, per split measured best) or when the
 // staged activations would not fit the LDS.  NVFP4_M16_{G,RB,KS,KZ,D,CP}
-// override the choice (tuning knobs; results change only by fp32 summation
-// order).
+// and NVFP4_M16_AW override the choice (tuning knobs; results change only by
+// fp32 summation order).
 constexpr int kSplitLines = 34;
 
 Plan make_plan(const GemmArgs& a, bool can_split) {
@@ -449,12 +516,14 @@ Plan make_plan(const GemmArgs& a, bool can_split) {
   pl.G = 1;
   const int e_g = env_int("NVFP4_M16_G", 0);
   if (e_g == 1 || e_g == 2 || e_g == 4) pl.G = e_g;
+  // up to 16 waves per workgroup with one row group per wave (<= 128 VGPRs), else 8
+  const int max_waves = pl.G == 1 ? 16 : 8;
   pl.RB = 8;
   const int e_rb = env_int("NVFP4_M16_RB", 0);
-  if (e_rb >= 1 && e_rb <= 8) pl.RB = e_rb;
+  if (e_rb >= 1 && e_rb <= max_waves) pl.RB = e_rb;
   pl.KS = 1;
   const int e_ks = env_int("NVFP4_M16_KS", 0);
-  if (e_ks >= 1 && e_ks <= 8 && e_ks * pl.RB <= 8) pl.KS = e_ks;
+  if (e_ks >= 1 && e_ks <= 8 && e_ks * pl.RB <= max_waves) pl.KS = e_ks;
   const int64_t waves_per_split = ((a.N + 16 * pl.G - 1) / (16 * pl.G)) * pl.KS;
   int KZ = 1;
   if (can_split) {
@@ -462,7 +531,9 @@ Plan make_plan(const GemmArgs& a, bool can_split) {
     const int e_kz = env_int("NVFP4_M16_KZ", 0);
     if (e_kz >= 1) KZ = e_kz < L ? e_kz : L;
   }
-  const int mls = max_ls(pl.RB * pl.KS * pl.G);
+  const bool aw = env_int("NVFP4_M16_AW", 1) == 1 && pl.G == 1 && pl.RB == 8 && pl.KS == 1 &&
+                  env_int("NVFP4_M16_CP", 0) != 2;
+  const int mls = aw ? 1 << 20 : max_ls(pl.RB * pl.KS * pl.G);  // AW stages no whole K range
   while ((L + KZ - 1) / KZ > mls) ++KZ;
   pl.LS = (L + KZ - 1) / KZ;
   pl.LS += pl.LS & (L > pl.LS ? 1 : 0);  // splits start on an even line (whole 128-byte runs)
@@ -471,6 +542,7 @@ Plan make_plan(const GemmArgs& a, bool can_split) {
   if (pl.D != 1 && pl.D != 2 && pl.D != 4) pl.D = 2;
   if (pl.G == 4 && pl.D == 4) pl.D = 2;  // would spill registers
   pl.CP = env_int("NVFP4_M16_CP", 0) == 2 ? 2 : 0;
+  pl.AW = env_int("NVFP4_M16_AW", 1) == 1 && pl.G == 1 && pl.RB == 8 && pl.KS == 1 && pl.CP == 0;
   return pl;
 }
 
@@ -490,7 +562,21 @@ template <int G, int D, int CP>
 hipError_t launch_gd(const GemmArgs& a, const Plan& pl, Split sp, hipStream_t stream) {
   const dim3 grid((unsigned)row_blocks(a, pl), (unsigned)pl.KZ);
   const int nw = pl.RB * pl.KS;
-  const uint32_t lds = lds_bytes(pl.LS, nw, G);  // >= the KS partial sums (nw * G KiB)
+  const uint32_t lds = lds_bytes(pl.LS, nw, G, pl.AW);  // >= the KS partial sums (nw * G KiB)
+  if constexpr (G == 1 && CP == 0) {
+    if (pl.AW) {
+      if (a.out_bf16) gemm_m16_kernel<G, D, CP, true, 512, true><<<grid, 64 * nw, lds, stream>>>(a, pl.KS, pl.LS, sp);
+      else gemm_m16_kernel<G, D, CP, false, 512, true><<<grid, 64 * nw, lds, stream>>>(a, pl.KS, pl.LS, sp);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (G == 1) {
+    if (nw > 8) {
+      if (a.out_bf16) gemm_m16_kernel<G, D, CP, true, 1024><<<grid, 64 * nw, lds, stream>>>(a, pl.KS, pl.LS, sp);
+      else gemm_m16_kernel<G, D, CP, false, 1024><<<grid, 64 * nw, lds, stream>>>(a, pl.KS, pl.LS, sp);
+      return hipGetLastError();
+    }
+  }
   if (a.out_bf16) gemm_m16_kernel<G, D, CP, true><<<grid, 64 * nw, lds, stream>>>(a, pl.KS, pl.LS, sp);
   else gemm_m16_kernel<G, D, CP, false><<<grid, 64 * nw, lds, stream>>>(a, pl.KS, pl.LS, sp);
   return hipGetLastError();
