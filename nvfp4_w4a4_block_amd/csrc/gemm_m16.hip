@@ -602,8 +602,9 @@ int64_t gemm_m16_workspace_bytes(const GemmArgs& a) {
 }
 
 // Any K that is a multiple of 128: with a large enough workspace the lines
-// are split over workgroups as needed; without one, the staged activations of
-// the whole K must fit the LDS (K <= 6272 with the default plan).
+// are split over workgroups as needed; without one, the default plan (shared
+// activation window) takes any K in one pass, and plans that stage the
+// activations of the whole K range need them to fit the LDS (K <= 6272).
 bool gemm_m16_supported(const GemmArgs& a) {
   if (a.M < 1 || a.M > 16 || a.K % kLine != 0) return false;
   const bool split = have_workspace(a) && a.workspace_bytes >= gemm_m16_workspace_bytes(a);

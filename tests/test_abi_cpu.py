@@ -89,6 +89,21 @@ def test_gemm_ws_validation(lib):
     assert ws(0, 256, 64, work=0, nbytes=0, ptrs=(0,) * 7) == B.NVFP4_OK
 
 
+def test_gemm_workspace_bytes_host_cases(lib):
+    """Shapes the split path never takes need no workspace (decided on the host, no HIP call):
+    one or two rows (the GEMV), more than 16 rows (the tiled path), K not a multiple of 128,
+    invalid shapes."""
+    f = lib.nvfp4_gemm_workspace_bytes
+    assert f(1, 25600, 5120) == 0
+    assert f(2, 25600, 5120) == 0
+    assert f(17, 25600, 5120) == 0
+    assert f(512, 5120, 25600) == 0
+    assert f(16, 25616, 5120) == 0
+    assert f(16, 25600, 0) == 0
+    assert f(16, 24, 5120) == 0
+    assert f(-1, 256, 64) == 0
+
+
 def test_empty_gemm_is_ok_without_pointers(lib):
     assert gemm(lib, 0, 32, 16, ptrs=(0,) * 7) == B.NVFP4_OK
     assert gemm(lib, 4, 32, 0, ptrs=(0,) * 7) == B.NVFP4_OK
