@@ -180,6 +180,27 @@ nvfp4_status nvfp4_gemm_ws(int64_t M, int64_t K, int64_t N,
                            void* out, nvfp4_dtype out_dt, void* workspace, int64_t workspace_bytes,
                            void* stream);
 
+/* NVFP4 W4A4 GEMM whose output is also emitted in NVFP4: the product of one
+ * layer of a prefill becomes the quantized activations of the next.
+ *   a_*, w_*, out, out_dt: as nvfp4_gemm (out is required).
+ *   y_global  in: device float, the static calibrated decode scale of the output.
+ *   y_codes   out: [M][N/2];  y_scales out: [M][N/16]: bit-identical to
+ *             nvfp4_quantize_act(out, out_dt, M, N, y_global, ...) applied to
+ *             the stored out (so bf16 outputs are quantized after rounding).
+ * N % 16 == 0 (the output's blocks run along N), else NVFP4_ERR_SHAPE.  For
+ * M > 16 with K a multiple of 1024 this is one kernel: the epilogue of the
+ * tiled GEMM quantizes each 16-column block of its tile while writing it, so
+ * the output is not read back; other shapes run the GEMM, then the
+ * quantization (two launches, same results).
+ * Cites: the page sections "Using NVFP4 quantization to accelerate
+ * Qwen3.6-27B inference" (weights and activations NVFP4) and "Reusing KV
+ * cache across agent turns" (a suffix prefill passes through every layer). */
+nvfp4_status nvfp4_gemm_quantize_output(int64_t M, int64_t K, int64_t N,
+                                        const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                                        const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                                        void* out, nvfp4_dtype out_dt, const float* y_global, uint8_t* y_codes,
+                                        uint8_t* y_scales, void* stream);
+
 /* Activation quantization and GEMM in one call: the decode step's
  * nvfp4_quantize_act + nvfp4_gemm.
  *   a         [M][K] raw activations in a_dt (NVFP4_F32 or NVFP4_BF16), device.

@@ -22,8 +22,8 @@ NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_DTYPE, NVF
 NVFP4_F32, NVFP4_BF16 = 0, 1
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 
-EXPORTS = ("nvfp4_abi_version", "nvfp4_act_global_scale", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_gemm_workspace_bytes",
-           "nvfp4_gemm_ws", "nvfp4_kv_fp8_decode", "nvfp4_kv_fp8_encode",
+EXPORTS = ("nvfp4_abi_version", "nvfp4_act_global_scale", "nvfp4_gemm", "nvfp4_gemm_ex",
+           "nvfp4_gemm_quantize_output", "nvfp4_gemm_workspace_bytes", "nvfp4_gemm_ws", "nvfp4_kv_fp8_decode", "nvfp4_kv_fp8_encode",
            "nvfp4_quantize_act",
            "nvfp4_quantize_gemm", "nvfp4_quantize_weights", "nvfp4_status_string", "nvfp4_tree_accept",
            "nvfp4_tree_verify")
@@ -51,6 +51,7 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, p]
     lib.nvfp4_gemm_ex.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, i32, p]
     lib.nvfp4_gemm_ws.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, p, i64, p]
+    lib.nvfp4_gemm_quantize_output.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, p, p, p, p]
     lib.nvfp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
     lib.nvfp4_gemm_workspace_bytes.restype = i64
     lib.nvfp4_quantize_gemm.argtypes = [i64, i64, i64, p, i32, p, p, p, p, p, i32, p, p, p]
@@ -60,6 +61,7 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_kv_fp8_decode.argtypes = [p, i64, p, p, i32, p]
     lib.nvfp4_tree_verify.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p, p, p, p, p, p]
     for f in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_gemm_ws",
+              "nvfp4_gemm_quantize_output",
               "nvfp4_quantize_gemm", "nvfp4_tree_accept", "nvfp4_tree_verify", "nvfp4_kv_fp8_encode",
               "nvfp4_kv_fp8_decode", "nvfp4_act_global_scale"):
         getattr(lib, f).restype = i32
@@ -205,6 +207,48 @@ def nvfp4_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: torch.Tensor,
                                 workspace.numel() if workspace is not None else 0, _stream(dev)),
            "nvfp4_gemm_ws")
     return out
+
+
+def nvfp4_gemm_quantize_output(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: torch.Tensor,
+                               w_codes: torch.Tensor, w_scales: torch.Tensor, g_w: torch.Tensor,
+                               g_y: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                               out: Optional[torch.Tensor] = None, y_codes: Optional[torch.Tensor] = None,
+                               y_scales: Optional[torch.Tensor] = None
+                               ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """NVFP4 product whose output is also quantized with the device scale g_y [1]: returns
+    (out [M, N], y_codes [M, N/2], y_scales [M, N/16])."""
+    if a_codes.dim() != 2 or w_codes.dim() != 2:
+        raise ValueError("codes must be 2-D")
+    M, K2 = a_codes.shape
+    N = w_codes.shape[0]
+    K = 2 * K2
+    if w_codes.shape[1] != K2 or a_scales.shape != (M, K // 16) or w_scales.shape != (N, K // 16):
+        raise ValueError("inconsistent operand shapes")
+    for t in (a_codes, a_scales, w_codes, w_scales):
+        if t.dtype != torch.uint8:
+            raise ValueError("codes and scales must be uint8")
+    for g in (g_a, g_w, g_y):
+        if g.dtype != torch.float32 or g.numel() != 1:
+            raise ValueError("tensor scales must be float32 tensors of one element")
+    dev = _dev(a_codes, a_scales, g_a, w_codes, w_scales, g_w, g_y)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    elif out.shape != (M, N) or out.dtype != out_dtype:
+        raise ValueError("out must be [M, N] of out_dtype")
+    if y_codes is None:
+        y_codes = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+    if y_scales is None:
+        y_scales = torch.empty((M, N // 16), dtype=torch.uint8, device=dev)
+    if y_codes.dtype != torch.uint8 or y_scales.dtype != torch.uint8 or \
+            y_codes.numel() != M * (N // 2) or y_scales.numel() != M * (N // 16):
+        raise ValueError("y_codes/y_scales must be uint8 of [M, N/2] / [M, N/16] elements")
+    _dev(a_codes, out, y_codes, y_scales)
+    _check(load().nvfp4_gemm_quantize_output(M, K, N, a_codes.data_ptr(), a_scales.data_ptr(), g_a.data_ptr(),
+                                             w_codes.data_ptr(), w_scales.data_ptr(), g_w.data_ptr(),
+                                             out.data_ptr(), _dt(out_dtype), g_y.data_ptr(), y_codes.data_ptr(),
+                                             y_scales.data_ptr(), _stream(dev)),
+           "nvfp4_gemm_quantize_output")
+    return out, y_codes, y_scales
 
 
 def nvfp4_quantize_gemm(a: torch.Tensor, g_a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,

@@ -41,7 +41,7 @@ const char* nvfp4_status_string(nvfp4_status s) {
   return "unknown status";
 }
 
-int nvfp4_abi_version(void) { return 6; }
+int nvfp4_abi_version(void) { return 7; }
 
 nvfp4_status nvfp4_quantize_weights(const void* w, nvfp4_dtype w_dt, int64_t N, int64_t K,
                                     uint8_t* w_codes, uint8_t* w_scales, float* w_global,
@@ -161,6 +161,47 @@ nvfp4_status nvfp4_gemm_ws(int64_t M, int64_t K, int64_t N,
                            void* stream) {
   return gemm_impl(M, K, N, a_codes, a_scales, a_global, w_codes, w_scales, w_global, out, out_dt,
                    NVFP4_PATH_AUTO, workspace, workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_gemm_quantize_output(int64_t M, int64_t K, int64_t N,
+                                        const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                                        const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                                        void* out, nvfp4_dtype out_dt, const float* y_global, uint8_t* y_codes,
+                                        uint8_t* y_scales, void* stream) {
+  if (!dtype_ok(out_dt)) return NVFP4_ERR_DTYPE;
+  if (!shape_ok(M, K) || !shape_ok(N, K) || !shape_ok(M, N > 0 ? N : 16) || N % 16 != 0) return NVFP4_ERR_SHAPE;
+  if (M > 0 && N >= kMaxElems / M) return NVFP4_ERR_SHAPE;
+  if ((M <= 16 ? (M + 15) / 16 : (M + 127) / 128) > kMaxGridY) return NVFP4_ERR_SHAPE;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!a_codes || !a_scales || !a_global || !w_codes || !w_scales || !w_global || !out || !y_global || !y_codes ||
+      !y_scales)
+    return NVFP4_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(out) || !aligned4(a_global) || !aligned4(w_global) || !aligned4(y_global) || !aligned16(y_codes) ||
+      !aligned16(y_scales))
+    return NVFP4_ERR_ALIGN;
+  nvfp4::GemmArgs g;
+  g.M = (int)M;
+  g.K = (int)K;
+  g.N = (int)N;
+  g.ac = a_codes;
+  g.as = a_scales;
+  g.ga = a_global;
+  g.wc = w_codes;
+  g.ws = w_scales;
+  g.gw = w_global;
+  g.out = out;
+  g.out_bf16 = out_dt == NVFP4_BF16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M > 16 && nvfp4::gemm_tiled_quant_out_supported(g)) {  // one kernel: quantized in the epilogue
+    g.y_global = y_global;
+    g.y_codes = y_codes;
+    g.y_scales = y_scales;
+    return from_hip(nvfp4::launch_gemm_tiled(g, s));
+  }
+  hipError_t e = M <= 16 ? nvfp4::launch_gemm_skinny(g, s) : nvfp4::launch_gemm_tiled(g, s);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(nvfp4::launch_quantize(out, g.out_bf16, M, N, y_global, y_codes, y_scales, s));
 }
 
 nvfp4_status nvfp4_quantize_gemm(int64_t M, int64_t K, int64_t N,

@@ -235,7 +235,7 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(h8_t a, h8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool QOUT>
 __global__ __launch_bounds__(64 * kWaves) void gemm_wg_tiled_kernel(GemmArgs p, int tiles_m, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
@@ -362,6 +362,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wg_tiled_kernel(GemmArgs p, 
   };
 
   const float gg = (*p.ga) * (*p.gw);
+  [[maybe_unused]] const float gy = QOUT ? *p.y_global : 0.0f;
 
   // Load pointers: codes run three steps ahead of the multiplies, scales one
   // group ahead; both continue into the next tile.
@@ -475,6 +476,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wg_tiled_kernel(GemmArgs p, 
     // order and stores it: elements 2w, 2w + 1 of lane l are rows
     // 8(w / 2) + 4(l / 32) + 2(w % 2) + 0..1, column l % 32 of the tile.
     f2_t* red = reinterpret_cast<f2_t*>(lds + kRedOff);
+    [[maybe_unused]] uint32_t qv[MT * NT];  // bf16 output quantization: this lane's two stored values per tile
 #pragma unroll
     for (int tix = 0; tix < MT * NT; ++tix) {
       const f32x16_t a = acc[tix / NT][tix % NT];
@@ -485,22 +487,96 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wg_tiled_kernel(GemmArgs p, 
 #pragma unroll
       for (int v = 1; v < kWaves; ++v) sum += red[(v * 8 + w) * 64 + lane];
       const int n = n0 + 32 * (tix % NT) + r32;
-      if (n < N) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int m = m0 + 32 * (tix / NT) + 8 * (w >> 1) + 4 * kq + 2 * (w & 1) + e;
-          if (m < M) {
-            const float v = sum[e] * gg;
-            const int64_t o = (int64_t)m * N + n;
-            if constexpr (OUT_BF16) {
-              reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(v);
-            } else {
-              reinterpret_cast<float*>(p.out)[o] = v;
-            }
+      for (int e = 0; e < 2; ++e) {
+        const int m = m0 + 32 * (tix / NT) + 8 * (w >> 1) + 4 * kq + 2 * (w & 1) + e;
+        const bool ok = n < N && m < M;
+        const float v = sum[e] * gg;
+        if constexpr (OUT_BF16) {
+          const uint16_t bits = f32_to_bf16_rne(v);
+          if (ok) reinterpret_cast<uint16_t*>(p.out)[(int64_t)m * N + n] = bits;
+          if constexpr (QOUT) {  // quantized after the tile, from LDS (below)
+            if (e == 0) qv[tix] = bits;
+            else qv[tix] |= (uint32_t)bits << 16;
+          }
+        } else {
+          if (ok) reinterpret_cast<float*>(p.out)[(int64_t)m * N + n] = v;
+        }
+        if constexpr (QOUT && !OUT_BF16) {
+          const float x = v;  // the value as stored
+          // The 16 lanes 16c .. 16c+15 of a half-wave hold one 16-column
+          // block of row m (N % 16 == 0: a block is wholly inside or wholly
+          // outside the matrix).  The same fp32 steps as every quantizer here:
+          // amax, s = (amax / 6) / g, scale byte, d = sv * g, inv = 1 / d,
+          // codes of x * inv; element 2j in the low nibble of byte j.
+          float amax = __builtin_fabsf(x);
+#pragma unroll
+          for (int sh = 1; sh < 16; sh <<= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, sh));
+          const float s = (gy == 0.0f) ? 0.0f : (amax / 6.0f) / gy;
+          const uint32_t sbyte = e4m3_from_nonneg(s);
+          const float d = e4m3_to_f32(sbyte) * gy;
+          const float inv = (d == 0.0f) ? 0.0f : 1.0f / d;
+          uint32_t word = e2m1_from_f32(x * inv) << (4 * (r32 & 7));
+#pragma unroll
+          for (int sh = 1; sh < 8; sh <<= 1) word |= __shfl_xor(word, sh);
+          if (ok) {
+            const int64_t blk = (int64_t)m * (N >> 4) + (n >> 4);
+            if ((r32 & 7) == 0) reinterpret_cast<uint32_t*>(p.y_codes)[2 * blk + ((r32 >> 3) & 1)] = word;
+            if ((r32 & 15) == 0) p.y_scales[blk] = (uint8_t)sbyte;
           }
         }
       }
       barrier_lds();
+    }
+    if constexpr (QOUT && OUT_BF16) {
+      // The tile's stored bf16 values, [64 rows][160 columns], staged in the
+      // reduction area, then quantized as quant_blocks_kernel quantizes them:
+      // two adjacent threads per 16-column block, eight values each, the same
+      // fp32 steps (amax, s = (amax / 6) / g, scale byte, d = sv * g, inv =
+      // 1 / d, codes of x * inv), element 2j in the low nibble of byte j.
+      uint16_t* stage = reinterpret_cast<uint16_t*>(lds + kRedOff);
+#pragma unroll
+      for (int tix = 0; tix < MT * NT; ++tix) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int row = 32 * (tix / NT) + 8 * (w >> 1) + 4 * kq + 2 * (w & 1) + e;
+          stage[row * BNW + 32 * (tix % NT) + r32] = (uint16_t)(qv[tix] >> (16 * e));
+        }
+      }
+      barrier_lds();
+      constexpr int kHalves = BMW * (BNW / 8);  // 1280 runs of 8 values
+#pragma unroll
+      for (int i = 0; i < (kHalves + 64 * kWaves - 1) / (64 * kWaves); ++i) {
+        const int hb = (int)threadIdx.x + 64 * kWaves * i;
+        const bool valid = hb < kHalves;
+        const int row = hb / (BNW / 8), rem = hb - row * (BNW / 8), blk = rem >> 1, half = rem & 1;
+        u4_t raw = u4_t{0u, 0u, 0u, 0u};
+        if (valid) raw = *reinterpret_cast<const u4_t*>(stage + row * BNW + 16 * blk + 8 * half);
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[2 * k] = __uint_as_float(raw[k] << 16);
+          x[2 * k + 1] = __uint_as_float(raw[k] & 0xFFFF0000u);
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[k]));
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));  // the block's other half: thread ^ 1
+        const float s = (gy == 0.0f) ? 0.0f : (amax / 6.0f) / gy;
+        const uint32_t sbyte = e4m3_from_nonneg(s);
+        const float d = e4m3_to_f32(sbyte) * gy;
+        const float inv = (d == 0.0f) ? 0.0f : 1.0f / d;
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) word |= e2m1_from_f32(x[k] * inv) << (4 * k);
+        const int m = m0 + row, n = n0 + 16 * blk;
+        if (valid && m < M && n < N) {
+          const int64_t b16 = (int64_t)m * (N >> 4) + (n >> 4);
+          reinterpret_cast<uint32_t*>(p.y_codes)[2 * b16 + half] = word;
+          if (half == 0) p.y_scales[b16] = (uint8_t)sbyte;
+        }
+      }
+      barrier_lds();  // the staging is read before the next tile reduces through the same LDS
     }
   }
 }
@@ -519,27 +595,38 @@ static int tiled_cus() {
   return cus[dev];
 }
 
-hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
+namespace {
+
+bool persistent_ok(const GemmArgs& a) {
   // buffer offsets are 32-bit: rows up to one tile past the end must stay below 2^31 bytes
   const int64_t rows = (int64_t)(a.M > a.N ? a.M : a.N) + BNW;
-  if (a.K % (kStepK * kGroup) == 0 && a.K > 0 && rows * (a.K / 2) < ((int64_t)1 << 31)) {
-    const int tiles_m = (a.M + BMW - 1) / BMW, tiles_n = (a.N + BNW - 1) / BNW;
-    const int total = tiles_m * tiles_n;
-    const int cus = tiled_cus();
-    const dim3 grid((unsigned)(total < cus ? total : cus));
-    // more than the default 64 KiB of dynamic LDS: raise the kernels' limit once
-    static const hipError_t attr = [] {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wg_tiled_kernel<true>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-      if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_wg_tiled_kernel<false>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-      return e;
-    }();
-    if (attr != hipSuccess) return attr;
-    if (a.out_bf16) gemm_wg_tiled_kernel<true><<<grid, 64 * kWaves, kLdsBytes, stream>>>(a, tiles_m, tiles_n);
-    else gemm_wg_tiled_kernel<false><<<grid, 64 * kWaves, kLdsBytes, stream>>>(a, tiles_m, tiles_n);
-    return hipGetLastError();
+  return a.K % (kStepK * kGroup) == 0 && a.K > 0 && rows * (a.K / 2) < ((int64_t)1 << 31);
+}
+
+template <bool OUT_BF16, bool QOUT>
+hipError_t launch_persistent(const GemmArgs& a, hipStream_t stream) {
+  const int tiles_m = (a.M + BMW - 1) / BMW, tiles_n = (a.N + BNW - 1) / BNW;
+  const int total = tiles_m * tiles_n;
+  const int cus = tiled_cus();
+  const dim3 grid((unsigned)(total < cus ? total : cus));
+  // more than the default 64 KiB of dynamic LDS: raise this kernel's limit once
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gemm_wg_tiled_kernel<OUT_BF16, QOUT>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  gemm_wg_tiled_kernel<OUT_BF16, QOUT><<<grid, 64 * kWaves, kLdsBytes, stream>>>(a, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_tiled_quant_out_supported(const GemmArgs& a) { return persistent_ok(a) && a.N % 16 == 0; }
+
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
+  if (persistent_ok(a)) {
+    const bool q = a.y_codes != nullptr && a.N % 16 == 0;
+    if (a.out_bf16) return q ? launch_persistent<true, true>(a, stream) : launch_persistent<true, false>(a, stream);
+    return q ? launch_persistent<false, true>(a, stream) : launch_persistent<false, false>(a, stream);
   }
   const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
   const bool k32 = a.K % 32 == 0;

@@ -46,6 +46,14 @@ struct GemmArgs {
   // again when the kernel ends.
   void* workspace = nullptr;
   int64_t workspace_bytes = 0;
+  // Output quantization (persistent tiled kernel only, N % 16 == 0): when
+  // y_codes is set, every 16-column block of each output row, rounded to the
+  // output dtype as stored, is also quantized with the decode scale *y_global
+  // exactly as quant_blocks_kernel would quantize the stored output, into
+  // y_codes [M][N/2] and y_scales [M][N/16].
+  const float* y_global = nullptr;
+  uint8_t* y_codes = nullptr;
+  uint8_t* y_scales = nullptr;
 };
 
 constexpr int kKeySlots = 64;  // argmax key slots per row
@@ -77,7 +85,10 @@ bool gemm_m16_supported(const GemmArgs& a);
 int64_t gemm_m16_workspace_bytes(const GemmArgs& a);
 hipError_t launch_gemm_m16(const GemmArgs& a, hipStream_t stream);
 
-// LDS-tiled MFMA path for large M.
+// LDS-tiled MFMA path for large M.  gemm_tiled_quant_out_supported() tells
+// whether launch_gemm_tiled() honours y_codes (the persistent kernel: K %
+// 1024 == 0, N % 16 == 0); launch_gemm_tiled() ignores y_codes otherwise.
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
+bool gemm_tiled_quant_out_supported(const GemmArgs& a);
 
 }  // namespace nvfp4

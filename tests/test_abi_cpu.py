@@ -42,7 +42,7 @@ def test_status_strings_and_version(lib):
     for s in range(6):
         assert B.status_string(s)
     assert B.status_string(99) == "unknown status"
-    assert lib.nvfp4_abi_version() == 6
+    assert lib.nvfp4_abi_version() == 7
 
 
 def gemm(lib, M, K, N, ptrs=(A16,) * 7, out_dt=B.NVFP4_BF16, path=B.PATH_AUTO):
@@ -87,6 +87,26 @@ def test_gemm_ws_validation(lib):
     assert ws(16, 256, 64, work=A16 + 8) == B.NVFP4_ERR_ALIGN
     assert ws(16, 256, 64, ptrs=(A16,) * 6 + (0,)) == B.NVFP4_ERR_NULL
     assert ws(0, 256, 64, work=0, nbytes=0, ptrs=(0,) * 7) == B.NVFP4_OK
+
+
+def test_gemm_quantize_output_validation(lib):
+    """nvfp4_gemm_quantize_output: nvfp4_gemm's rules plus N % 16 == 0 and the output-quantization
+    pointers (scale 4-byte aligned, codes and scales 16-byte aligned)."""
+    def qo(M, K, N, out_dt=B.NVFP4_BF16, ptrs=(A16,) * 10):
+        ac, asc, ga, wc, wsc, gw, out, gy, yc, ys = ptrs
+        return lib.nvfp4_gemm_quantize_output(M, K, N, ac, asc, ga, wc, wsc, gw, out, out_dt, gy, yc, ys, None)
+    assert qo(64, 256, 64, out_dt=5) == B.NVFP4_ERR_DTYPE
+    assert qo(64, 256, 40) == B.NVFP4_ERR_SHAPE      # output blocks run along N
+    assert qo(64, 24, 64) == B.NVFP4_ERR_SHAPE
+    assert qo(0, 256, 64, ptrs=(0,) * 10) == B.NVFP4_OK
+    for k in range(10):
+        ptrs = [A16] * 10
+        ptrs[k] = 0
+        assert qo(64, 256, 64, ptrs=tuple(ptrs)) == B.NVFP4_ERR_NULL, k
+    for k, off in ((7, 2), (8, 8), (9, 4), (6, 8)):
+        ptrs = [A16] * 10
+        ptrs[k] = A16 + off
+        assert qo(64, 256, 64, ptrs=tuple(ptrs)) == B.NVFP4_ERR_ALIGN, k
 
 
 def test_gemm_workspace_bytes_host_cases(lib):

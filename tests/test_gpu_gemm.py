@@ -259,9 +259,12 @@ def test_prefill_chain_up_then_down():
     wc1, ws1, gw1_d = B.nvfp4_quantize_weights(U.dev_f32(inp.W))
     wc2, ws2, gw2_d = B.nvfp4_quantize_weights(U.dev_f32(inp.W2))
     ac1, as1 = B.nvfp4_quantize_act(U.dev_acts(inp), U.scalar(g1))
-    y1 = B.nvfp4_gemm(ac1, as1, U.scalar(g1), wc1, ws1, gw1_d, out_dtype=torch.bfloat16)
-    ac2, as2 = B.nvfp4_quantize_act(y1, U.scalar(g2))
+    y1, ac2, as2 = B.nvfp4_gemm_quantize_output(ac1, as1, U.scalar(g1), wc1, ws1, gw1_d, U.scalar(g2),
+                                                out_dtype=torch.bfloat16)
     y2 = B.nvfp4_gemm(ac2, as2, U.scalar(g2), wc2, ws2, gw2_d, out_dtype=torch.bfloat16)
+    # the fused re-quantization equals quantizing the stored Y1 in a separate launch
+    qc, qs = B.nvfp4_quantize_act(y1, U.scalar(g2))
+    assert torch.equal(qc, ac2) and torch.equal(qs, as2)
 
     y1h = U.host(y1)
     U.assert_within(y1h[rows], C1r, T1r, "GEMM1 sampled rows")
