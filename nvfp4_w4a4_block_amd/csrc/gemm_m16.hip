@@ -82,9 +82,16 @@ constexpr int kAwThreads = 512;                          // AW workgroups: 8 wav
 static_assert(16 * kWin * kLine / 16 == kAwThreads, "one 16-element block per thread and window");
 
 __host__ __device__ constexpr uint32_t a_region(bool aw, int LS) { return aw ? 2u * kWinSlot : alds_bytes(LS); }
-// LDS of a workgroup: the activations, then one scale slot per wave and row group.
-__host__ __device__ constexpr uint32_t lds_bytes(int LS, int waves, int G, bool aw = false) {
-  return a_region(aw, LS) + (uint32_t)waves * (uint32_t)G * kScaleSlot;
+// Whole-range weight scales (SB, with AW): each wave stages the scale bytes of
+// its 16 rows for all the workgroup's lines once, in 16-byte chunks of two
+// lines; row stride 16 ceil(LS / 2) + 4 bytes (whole chunks, and an odd
+// number of words: the 16 rows of a quarter-wave hit distinct banks).
+constexpr int kSbMaxLines = 64;        // lines whose scales one wave stages (8 loads per lane)
+constexpr int kSbMaxLds = 160 * 1024;  // LDS a workgroup may allocate on gfx950 (static included)
+__host__ __device__ constexpr uint32_t sb_stride(int LS) { return 16u * (((uint32_t)LS + 1u) >> 1) + 4u; }
+// LDS of a workgroup: the activations, then the weight scales of every wave.
+__host__ __device__ constexpr uint32_t lds_bytes(int LS, int waves, int G, bool aw = false, bool sb = false) {
+  return a_region(aw, LS) + (sb ? (uint32_t)waves * 16u * sb_stride(LS) : (uint32_t)waves * (uint32_t)G * kScaleSlot);
 }
 
 // Workgroup barrier for LDS traffic only: this wave's LDS operations are done,
@@ -106,6 +113,7 @@ struct Plan {
   int D;   // pairs of lines of weight loads in flight per wave
   int CP;  // cache policy of the weight loads (2: non-temporal)
   bool AW; // shared activation window (G = 1, RB = 8, KS = 1)
+  bool SB; // with AW: each wave stages its weight scales for all its lines once (LS <= 64)
 };
 
 struct Split {
@@ -113,7 +121,7 @@ struct Split {
   uint32_t* cnt;  // [row blocks] arrival counters, zero between calls
 };
 
-template <int G, int D, int CP, bool OUT_BF16, int MAXT = 512, bool AW = false>
+template <int G, int D, int CP, bool OUT_BF16, int MAXT = 512, bool AW = false, bool SB = false>
 __global__ __launch_bounds__(MAXT) void gemm_m16_kernel(GemmArgs p, int KS, int LS, Split sp) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_m16[];
   const int lane = threadIdx.x & 63;
@@ -173,7 +181,8 @@ __global__ __launch_bounds__(MAXT) void gemm_m16_kernel(GemmArgs p, int KS, int 
     for (int g = 0; g < G; ++g)
       sb[g] = __builtin_amdgcn_raw_buffer_load_b128(ws, ok ? sb_off + 16u * g * srow + 8u * (uint32_t)(l0 + 2 * ub) : kOOB, 0, CP);
   };
-  uint8_t* const w_slot = lds_m16 + a_region(AW, LS) + (uint32_t)wave * G * kScaleSlot + 64u * (uint32_t)j;
+  uint8_t* const w_slot = SB ? lds_m16 + a_region(AW, LS) + ((uint32_t)wave * 16u + (uint32_t)j) * sb_stride(LS)
+                             : lds_m16 + a_region(AW, LS) + (uint32_t)wave * G * kScaleSlot + 64u * (uint32_t)j;
   auto park_scales = [&](const u4_t (&sb)[G]) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -184,8 +193,32 @@ __global__ __launch_bounds__(MAXT) void gemm_m16_kernel(GemmArgs p, int KS, int 
   };
 
   u4_t sX[G], sY[G];
-  load_scales(u0, sX);
-  load_scales(u0 + 4, sY);
+  if constexpr (SB) {
+    // this wave's 16 rows x lines [l0, l0 + Lr) of scale bytes: chunk c of row
+    // r (16 bytes, lines 2c and 2c + 1) -> slot row r at 16 c (as dwords)
+    const uint32_t nch = (uint32_t)(Lr + 1) >> 1, total = 16u * nch;
+    u4_t v[8];
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const uint32_t c = (uint32_t)lane + 64u * s8;
+      const uint32_t r = c / nch, k = c - r * nch;
+      v[s8] = __builtin_amdgcn_raw_buffer_load_b128(
+          ws, c < total ? (row0 + r) * srow + 8u * (uint32_t)l0 + 16u * k : kOOB, 0, 0);
+    }
+    uint8_t* const slot0 = lds_m16 + a_region(AW, LS) + (uint32_t)wave * 16u * sb_stride(LS);
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const uint32_t c = (uint32_t)lane + 64u * s8;
+      const uint32_t r = c / nch, k = c - r * nch;
+      if (c < total) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(slot0 + r * sb_stride(LS) + 16u * k + 4u * i) = v[s8][i];
+      }
+    }
+  } else {
+    load_scales(u0, sX);
+    load_scales(u0 + 4, sY);
+  }
   __builtin_amdgcn_sched_barrier(0);
   Pair<G> buf[D];
 #pragma unroll
@@ -300,7 +333,13 @@ __global__ __launch_bounds__(MAXT) void gemm_m16_kernel(GemmArgs p, int KS, int 
       }
       h2_t sw[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) sw[g] = e4m3x2_to_h2(w_scale(g, 2 * p + h));
+      for (int g = 0; g < G; ++g) {
+        if constexpr (SB) {
+          sw[g] = e4m3x2_to_h2(*reinterpret_cast<const uint16_t*>(w_slot + 8u * (uint32_t)t + 2u * (uint32_t)q));
+        } else {
+          sw[g] = e4m3x2_to_h2(w_scale(g, 2 * p + h));
+        }
+      }
 #pragma unroll
       for (int pc = 0; pc < 4; ++pc) {
 #pragma unroll
@@ -316,9 +355,11 @@ __global__ __launch_bounds__(MAXT) void gemm_m16_kernel(GemmArgs p, int KS, int 
   // holds pair ub + p.  Two blocks per iteration alternate the scale
   // registers: park block k, request block k + 2, compute block k.
   auto block = [&](int ub, u4_t (&sb)[G]) {
-    park_scales(sb);
-    load_scales(ub + 8, sb);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!SB) {
+      park_scales(sb);
+      load_scales(ub + 8, sb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       if constexpr (AW) {
@@ -496,17 +537,21 @@ constexpr int max_ls(int slots) {
   return (int)(((uint32_t)kMaxLdsM16 / 16u - 4u * kScaleSlot / 64u * (uint32_t)slots - 20u) / 72u);
 }
 static_assert(lds_bytes(max_ls(8), 8, 1) <= (uint32_t)kMaxLdsM16 && max_ls(32) >= 1, "LDS budget");
+// the most dynamic LDS an SB launch asks for, well below the hardware limit
+constexpr int kSbLds = (int)lds_bytes(kSbMaxLines, 8, 1, true, true);
+static_assert(kSbLds + 1024 <= kSbMaxLds, "SB LDS budget");
 
 // Launch plan, from a sweep over G x RB x KS x KZ x D x AW on MI355X at the
 // LM head (16 x 5120 x 151936) and the tree-verification down-projection (16 x
 // 25600 x 5120): one 16-row group per wave, eight waves with distinct rows per
-// workgroup sharing one dequantized activation window (AW), two pairs of lines
-// in flight, cached loads.  K
+// workgroup sharing one dequantized activation window (AW), each wave's weight
+// scales for all its lines staged once (SB), two pairs of lines in flight,
+// cached loads.  K
 // is split over workgroups when the rows alone give fewer than ~4 waves per
 // CU (about 34 lines, 4352 K-elements, per split measured best) or when the
 // staged activations would not fit the LDS.  NVFP4_M16_{G,RB,KS,KZ,D,CP}
-// and NVFP4_M16_AW override the choice (tuning knobs; results change only by
-// fp32 summation order).
+// NVFP4_M16_AW and NVFP4_M16_SB override the choice (tuning knobs; results
+// change only by fp32 summation order).
 constexpr int kSplitLines = 34;
 
 Plan make_plan(const GemmArgs& a, bool can_split) {
@@ -543,6 +588,7 @@ Plan make_plan(const GemmArgs& a, bool can_split) {
   if (pl.G == 4 && pl.D == 4) pl.D = 2;  // would spill registers
   pl.CP = env_int("NVFP4_M16_CP", 0) == 2 ? 2 : 0;
   pl.AW = env_int("NVFP4_M16_AW", 1) == 1 && pl.G == 1 && pl.RB == 8 && pl.KS == 1 && pl.CP == 0;
+  pl.SB = pl.AW && pl.LS <= kSbMaxLines && env_int("NVFP4_M16_SB", 1) == 1;
   return pl;
 }
 
@@ -562,8 +608,22 @@ template <int G, int D, int CP>
 hipError_t launch_gd(const GemmArgs& a, const Plan& pl, Split sp, hipStream_t stream) {
   const dim3 grid((unsigned)row_blocks(a, pl), (unsigned)pl.KZ);
   const int nw = pl.RB * pl.KS;
-  const uint32_t lds = lds_bytes(pl.LS, nw, G, pl.AW);  // >= the KS partial sums (nw * G KiB)
+  const uint32_t lds = lds_bytes(pl.LS, nw, G, pl.AW, pl.SB);  // >= the KS partial sums (nw * G KiB)
   if constexpr (G == 1 && CP == 0) {
+    if (pl.SB) {
+      static const hipError_t attr = [] {  // may exceed the default 64 KiB of dynamic LDS
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_m16_kernel<G, D, CP, true, 512, true, true>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, kSbLds);
+        if (e == hipSuccess)
+          e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_m16_kernel<G, D, CP, false, 512, true, true>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kSbLds);
+        return e;
+      }();
+      if (attr != hipSuccess) return attr;
+      if (a.out_bf16) gemm_m16_kernel<G, D, CP, true, 512, true, true><<<grid, 64 * nw, lds, stream>>>(a, pl.KS, pl.LS, sp);
+      else gemm_m16_kernel<G, D, CP, false, 512, true, true><<<grid, 64 * nw, lds, stream>>>(a, pl.KS, pl.LS, sp);
+      return hipGetLastError();
+    }
     if (pl.AW) {
       if (a.out_bf16) gemm_m16_kernel<G, D, CP, true, 512, true><<<grid, 64 * nw, lds, stream>>>(a, pl.KS, pl.LS, sp);
       else gemm_m16_kernel<G, D, CP, false, 512, true><<<grid, 64 * nw, lds, stream>>>(a, pl.KS, pl.LS, sp);

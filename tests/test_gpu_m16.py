@@ -23,7 +23,7 @@ from oracle import quant as Q
 pytestmark = pytest.mark.gpu
 
 KNOBS = ("NVFP4_M16_G", "NVFP4_M16_RB", "NVFP4_M16_KS", "NVFP4_M16_KZ", "NVFP4_M16_D", "NVFP4_M16_CP",
-         "NVFP4_M16_AW")
+         "NVFP4_M16_AW", "NVFP4_M16_SB")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -77,12 +77,14 @@ def test_m16_with_and_without_workspace(M, K, N):
 
 # Launch plans forced through the tuning knobs: row groups per wave (G), row blocks (RB) and K
 # slices (KS) per workgroup, K splits over workgroups (KZ), loads in flight (D), cache policy
-# (CP), activations dequantized once per workgroup into a shared f16 window (AW).
+# (CP), activations dequantized once per workgroup into a shared f16 window (AW), weight scales
+# of the whole K range staged once per wave (SB).
 PLANS = [dict(G=1, RB=1, KS=1, KZ=1, D=1), dict(G=4, RB=2, KS=4, KZ=1, D=2), dict(G=2, RB=1, KS=8, KZ=3, D=2),
          dict(G=1, RB=8, KS=1, KZ=7, D=4, CP=0), dict(G=4, RB=1, KS=2, KZ=13, D=1), dict(G=2, RB=4, KS=2, KZ=40, D=2, CP=2),
          dict(G=1, RB=8, KS=1, KZ=1, D=4), dict(G=1, RB=16, KS=1, KZ=5, D=2), dict(G=1, RB=8, KS=2, KZ=2, D=1),
          dict(G=1, RB=8, KS=1, KZ=1, D=2, AW=1), dict(G=1, RB=8, KS=1, KZ=3, D=1, AW=1),
-         dict(G=1, RB=8, KS=1, KZ=7, D=4, AW=1)]
+         dict(G=1, RB=8, KS=1, KZ=7, D=4, AW=1), dict(G=1, RB=8, KS=1, KZ=1, D=2, AW=1, SB=1),
+         dict(G=1, RB=8, KS=1, KZ=3, D=1, AW=1, SB=1), dict(G=1, RB=8, KS=1, KZ=5, D=4, AW=1, SB=1)]
 
 
 @pytest.mark.parametrize("plan", PLANS, ids=lambda p: "-".join(f"{k}{v}" for k, v in p.items()))
