@@ -671,6 +671,19 @@ bool gemm_m16_supported(const GemmArgs& a) {
   return split || make_plan(a, false).KZ == 1;
 }
 
+// The weight-streaming GEMM picks this kernel unless, with no workspace to
+// split K, it would leave most CUs idle on a long K (fewer than half as many
+// workgroups as CUs and more than two splits' worth of lines: the tree-
+// verification down-projection, 5120 x 25600, runs 67 us unsplit here against
+// 31 us in the older skinny kernel and 21 us split).
+bool gemm_m16_preferred(const GemmArgs& a) {
+  if (!gemm_m16_supported(a)) return false;
+  const bool split = have_workspace(a) && a.workspace_bytes >= gemm_m16_workspace_bytes(a);
+  if (split) return true;
+  const Plan pl = make_plan(a, false);
+  return !(row_blocks(a, pl) * 2 < device_cus() && a.K / kLine > 2 * kSplitLines);
+}
+
 hipError_t launch_gemm_m16(const GemmArgs& a, hipStream_t stream) {
   const bool split = have_workspace(a) && a.workspace_bytes >= gemm_m16_workspace_bytes(a);
   const Plan pl = make_plan(a, split);

@@ -920,7 +920,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   // are tuning knobs.
   const int e_gemv = env_int("NVFP4_GEMV", 3);
   if (e_gemv == 3 && gemv_fp4_supported(a)) return launch_gemv_fp4(a, stream);
-  if (a.M >= 3 && a.M <= 16 && env_int("NVFP4_M16", 1) != 0 && gemm_m16_supported(a)) return launch_gemm_m16(a, stream);
+  if (a.M >= 3 && a.M <= 16 && env_int("NVFP4_M16", 1) != 0 && gemm_m16_preferred(a)) return launch_gemm_m16(a, stream);
   if (e_gemv >= 2 && a.M <= 2 && a.K >= 2048 && a.K % 256 == 0) {
     int e_w = env_int("NVFP4_GEMV_W", 4);
     if (e_w != 4 && e_w != 8) e_w = 4;
