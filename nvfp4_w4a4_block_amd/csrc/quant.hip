@@ -44,13 +44,17 @@ __global__ __launch_bounds__(kQuantThreads) void quant_blocks_kernel(
     uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   const int64_t t = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
   const bool valid = t < n8;
+  // Lanes past the end read the first run (n8 > 0) and use zeros; without a
+  // branch around the load, and with the tensor scale fetched by a vector load
+  // issued right behind it, the two memory round trips overlap (a scalar load
+  // of the scale was waited for before the data load could start).
   float v[8];
-  if (valid) {
-    load8(x + t * 8, v);
-  } else {
+  load8(x + (valid ? t : 0) * 8, v);
+  const __amdgpu_buffer_rsrc_t gr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(g_ptr), (short)0, 4, 0x00020000);
+  const float g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, 0, 0, 0));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-  }
+  for (int i = 0; i < 8; ++i) v[i] = valid ? v[i] : 0.0f;
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
@@ -58,7 +62,6 @@ __global__ __launch_bounds__(kQuantThreads) void quant_blocks_kernel(
   // pair are valid or both are not; every lane takes part in the exchange.
   amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1));
 
-  const float g = *g_ptr;
   const float s = (g == 0.0f) ? 0.0f : (amax / 6.0f) / g;
   const uint32_t sb = e4m3_from_nonneg(s);
   const float d = e4m3_to_f32(sb) * g;
