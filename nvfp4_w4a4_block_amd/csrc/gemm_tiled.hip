@@ -178,12 +178,18 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(GemmArgs p) {
 // buffers and read as zeros.
 //
 // Schedule of step g: wait for this wave's loads of step g + 1, barrier (no
-// memory fence), read step g + 1's codes and scale bytes from LDS into the
-// other register set, issue the loads of step g + 3 into the slot step g used
+// memory fence), issue the loads of step g + 3 into the slot step g used
 // (every wave is past its reads) and, at a group start, the next scale group;
-// then multiply step g.  LDS latency hides behind the multiplies.
+// then multiply step g with the LDS reads of step g + 1's codes and scale
+// bytes (into the other register set) spread among its matrix instructions.
+// Reading them all right after the barrier stalled every wave at once on LDS
+// issue (the eight waves' reads arrive together); spread out they wait about a
+// third as long.  The step loop is unrolled by a scale group (4 steps), so each
+// step's expected wait count is a constant; anything else (a tile or stream
+// boundary) waits for all loads.
 // ---------------------------------------------------------------------------
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+template <int P> struct StepPos { static constexpr int value = P; };  // step index & 3
 
 constexpr int MT = 2, NT = 5;                // 32 x 32 MFMA tiles per workgroup tile
 constexpr int FT = MT + NT;                  // MFMA operand tiles
@@ -344,9 +350,11 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wg_tiled_kernel(GemmArgs p, 
     for (int t = 0; t < FT; ++t) o.s[t] = ss[t * 2 * kScaleTile];
   };
   auto multiply = [&](const Ops& o, f32x16_t (&acc)[MT][NT]) {
+    // E4M3 scale byte -> f16, exact (every finite E4M3 value is an f16 value);
+    // one conversion, the packed multiplies broadcast its low half.
     _Float16 sv[FT];
 #pragma unroll
-    for (int t = 0; t < FT; ++t) sv[t] = (_Float16)e4m3_to_f32(o.s[t]);
+    for (int t = 0; t < FT; ++t) sv[t] = (_Float16)__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(o.s[t], 1.0f, false)[0];
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
       h8_t af[MT];
@@ -358,6 +366,14 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wg_tiled_kernel(GemmArgs p, 
 #pragma unroll
         for (int ti = 0; ti < MT; ++ti) acc[ti][j] = mfma32x32x16(af[ti], bf, acc[ti][j]);
       }
+    }
+    // Interleave: each matrix instruction followed by (at first) one LDS read
+    // of the next step and a run of dequantization.
+#pragma unroll
+    for (int q = 0; q < 2 * MT * NT; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
+      if (q < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);           // VALU
     }
   };
 
@@ -418,22 +434,30 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wg_tiled_kernel(GemmArgs p, 
   // Top of step g: make step g + 1's operands ready in `nxt` and keep the
   // loads three steps ahead.  i is g's index inside its tile, it its tile.
   int slot = 0, sb = 0, g = 0;
-  auto advance = [&](int i, int it, Ops& nxt) {
+  auto advance = [&](auto pos, int i, int it, Ops& nxt) {
+    constexpr int P = decltype(pos)::value;  // == i & 3
     const int ni = (i + 1 == steps) ? 0 : i + 1;
     const int nslot = slot == 2 ? 0 : slot + 1;
     const int nsb = (ni & 3) == 0 ? sb ^ 1 : sb;
     if (g + 1 < total_steps) {
-      // After a tile's epilogue its output stores are outstanding too: wait for all.
-      wait_vm(i == 0 && it > 0 ? 0 : s_prev2 + c_prev1 + s_prev1);
+      // Loads issued after step g + 1's codes: the scale group of the step
+      // before last (P == 2), the last step's codes, the last step's scale
+      // group (P == 1).  After a tile's epilogue its output stores are
+      // outstanding too, and near the end of the stream fewer loads were
+      // issued: there (any other count) wait for all.
+      const int nw = i == 0 && it > 0 ? 0 : s_prev2 + c_prev1 + s_prev1;
+      constexpr int off = (P == 1 || P == 2) ? kScaleLoads : 0;
+      if (nw == 4 + off) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 + off));
+      else if (nw == 3 + off) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 + off));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       barrier_lds();
-      read_ops(nslot, nsb, ni, nxt);
       int c_cur = 0, s_cur = 0;
       if (g + 3 < total_steps) {
         issue_codes(c_i, slot);
         advance_codes();
         c_cur = n_code;
       }
-      if ((i & 3) == 0 && s_valid) {
+      if (P == 0 && s_valid) {
         issue_scales(s_gi, sb ^ 1);
         advance_scales();
         s_cur = kScaleLoads;
@@ -442,6 +466,10 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wg_tiled_kernel(GemmArgs p, 
       s_prev1 = s_cur;
       c_prev1 = c_cur;
     }
+    // Step g + 1's operands (none are used after the last step: there the
+    // read is of a slot no load writes any more).  The slots loaded above are
+    // not the ones read here.
+    read_ops(nslot, nsb, ni, nxt);
     slot = nslot;
     sb = nsb;
     ++g;
@@ -458,14 +486,18 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wg_tiled_kernel(GemmArgs p, 
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[ti][j][e] = 0.0f;
 
-    // steps is even: every tile starts with its operands in opa
-    for (int i = 0; i < steps; i += 2) {
-      advance(i, it, opb);
-      __builtin_amdgcn_sched_barrier(0);
+    // steps is a multiple of 4: every tile starts with its operands in opa
+    for (int i = 0; i < steps; i += 4) {
+      advance(StepPos<0>{}, i, it, opb);
       multiply(opa, acc);
       __builtin_amdgcn_sched_barrier(0);
-      advance(i + 1, it, opa);
+      advance(StepPos<1>{}, i + 1, it, opa);
+      multiply(opb, acc);
       __builtin_amdgcn_sched_barrier(0);
+      advance(StepPos<2>{}, i + 2, it, opb);
+      multiply(opa, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      advance(StepPos<3>{}, i + 3, it, opa);
       multiply(opb, acc);
       __builtin_amdgcn_sched_barrier(0);
     }
