@@ -237,6 +237,12 @@ __device__ __forceinline__ void barrier_lds() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// E4M3FN byte (finite) -> f16, exact, one instruction (every finite E4M3
+// value, subnormals included, is an f16 value; unit scale).
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t byte) {
+  return (_Float16)__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(byte, 1.0f, false)[0];
+}
+
 __device__ __forceinline__ f32x16_t mfma32x32x16(h8_t a, h8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
@@ -350,11 +356,10 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wg_tiled_kernel(GemmArgs p, 
     for (int t = 0; t < FT; ++t) o.s[t] = ss[t * 2 * kScaleTile];
   };
   auto multiply = [&](const Ops& o, f32x16_t (&acc)[MT][NT]) {
-    // E4M3 scale byte -> f16, exact (every finite E4M3 value is an f16 value);
-    // one conversion, the packed multiplies broadcast its low half.
+    // one conversion per scale byte; the packed multiplies broadcast its low half
     _Float16 sv[FT];
 #pragma unroll
-    for (int t = 0; t < FT; ++t) sv[t] = (_Float16)__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(o.s[t], 1.0f, false)[0];
+    for (int t = 0; t < FT; ++t) sv[t] = e4m3_to_f16(o.s[t]);
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
       h8_t af[MT];
