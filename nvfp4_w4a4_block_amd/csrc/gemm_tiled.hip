@@ -603,9 +603,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_wg_tiled_kernel(GemmArgs p, 
         const uint32_t sbyte = e4m3_from_nonneg(s);
         const float d = e4m3_to_f32(sbyte) * gy;
         const float inv = (d == 0.0f) ? 0.0f : 1.0f / d;
-        uint32_t word = 0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) word |= e2m1_from_f32(x[k] * inv) << (4 * k);
+        for (int k = 0; k < 8; ++k) x[k] *= inv;
+        const uint32_t word = e2m1x8_from_f32(x);
         const int m = m0 + row, n = n0 + 16 * blk;
         if (valid && m < M && n < N) {
           const int64_t b16 = (int64_t)m * (N >> 4) + (n >> 4);

@@ -66,9 +66,9 @@ __global__ __launch_bounds__(kQuantThreads) void quant_blocks_kernel(
   const uint32_t sb = e4m3_from_nonneg(s);
   const float d = e4m3_to_f32(sb) * g;
   const float inv = (d == 0.0f) ? 0.0f : 1.0f / d;
-  uint32_t word = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) word |= e2m1_from_f32(v[i] * inv) << (4 * i);
+  for (int i = 0; i < 8; ++i) v[i] *= inv;
+  const uint32_t word = e2m1x8_from_f32(v);
   if (valid) {
     codes[t] = word;
     if ((t & 1) == 0) scales[t >> 1] = (uint8_t)sb;

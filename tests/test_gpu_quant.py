@@ -105,6 +105,41 @@ def test_scale_extremes_and_saturation():
         np.testing.assert_array_equal(codes.cpu().numpy(), p, err_msg=f"g={g}")
 
 
+def test_e2m1_decision_points():
+    """Every E2M1 decision point (the midpoints .25, .75, 1.25, 1.75, 2.5, 3.5 and 5 between
+    neighbouring magnitudes), one fp32 ulp on either side, both signs, signed zeros, fp32
+    subnormals and values just past 6, each in a block whose largest magnitude is 6 under g = 1:
+    the block scale is then exactly 1 and every value is encoded as it is (round to nearest,
+    ties to the even code, saturation at 6)."""
+    f32 = np.float32
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    vals = []
+    for m in mids:
+        m = f32(m)
+        vals += [np.nextafter(m, f32(0)), m, np.nextafter(m, f32(np.inf))]
+    vals += [0.0, 1e-38, 1e-45, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    vals = np.array(vals, f32)
+    vals = np.concatenate([vals, -vals, np.array([-0.0], f32)])
+    blocks = []
+    for i in range(0, len(vals), 15):
+        blk = np.full(16, f32(0), f32)
+        chunk = vals[i:i + 15]
+        blk[:len(chunk)] = chunk
+        blk[15] = f32(6.0)
+        blocks.append(blk)
+    # values past 6 in a block whose scale still rounds to 1: they saturate to code 7
+    blocks.append(np.array([6.2, -6.2, 6.1, 0.3] + [0.0] * 12, f32))
+    x = np.concatenate(blocks).reshape(1, -1)
+    pad = (-x.shape[1]) % 64
+    x = np.concatenate([x, np.zeros((1, pad), f32)], axis=1)
+    g = f32(1.0)
+    codes, scales = B.nvfp4_quantize_act(U.dev_f32(x), U.scalar(g))
+    p, s = Q.quantize_packed(x, g)
+    np.testing.assert_array_equal(scales.cpu().numpy(), s)
+    np.testing.assert_array_equal(codes.cpu().numpy(), p)
+    assert int(s[0, 0]) == 0x38  # E4M3 1.0: the values above were encoded unscaled
+
+
 def test_zero_tensor_and_empty():
     w = torch.zeros((32, 64), dtype=torch.float32, device=U.DEV)
     codes, scales, g = B.nvfp4_quantize_weights(w)
