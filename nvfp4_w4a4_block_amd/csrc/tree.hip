@@ -57,9 +57,15 @@ __global__ __launch_bounds__(1024) void tree_accept_kernel(int n, const int32_t*
                                                            const int32_t* greedy_in, uint64_t* keys,
                                                            int32_t* greedy_out, int32_t* result) {
   __shared__ uint64_t kbest[kKeySlots * 16];
-  __shared__ int32_t g[64], par[64], dr[64], depth[64];
-  __shared__ uint8_t ok[64];
   const int t = threadIdx.x;
+  // Node inputs first, so that their loads overlap the key fold: lane v of
+  // wave 0 holds node v's parent, draft token and greedy token.
+  int32_t par = -1, dr = 0, gv = 0;
+  if (t < n) {
+    par = parent[t];
+    dr = draft[t];
+    if (!keys) gv = greedy_in[t];
+  }
   if (keys) {
     // thread t = slot * 16 + row holds one key; rows fold over the slots in LDS
     kbest[t] = keys[t];
@@ -69,36 +75,44 @@ __global__ __launch_bounds__(1024) void tree_accept_kernel(int n, const int32_t*
       if (t < half * 16) kbest[t] = kbest[t] > kbest[t + half * 16] ? kbest[t] : kbest[t + half * 16];
       __syncthreads();
     }
+    if (t < n) gv = (int32_t)(0xFFFFFFFFu - (uint32_t)kbest[t]);
   }
-  if (t < n) {
-    g[t] = keys ? (int32_t)(0xFFFFFFFFu - (uint32_t)kbest[t]) : greedy_in[t];
-    par[t] = parent[t];
-    dr[t] = draft[t];
-    if (greedy_out) greedy_out[t] = g[t];
+  if (t >= 64) return;  // no barrier follows
+  if (greedy_out && t < n) greedy_out[t] = gv;
+  // The walk in node order, in scalar registers: node u reads its parent's
+  // acceptance bit, depth and greedy token across lanes.
+  uint64_t okm = 1;  // bit v: node v accepted (the root is)
+  int32_t depth_v = 0;  // lane v: depth of node v
+  int end = 0, dend = 0;
+  for (int u = 1; u < n; ++u) {
+    const int pu = __builtin_amdgcn_readlane(par, u);
+    const bool valid = pu >= 0 && pu < u;
+    const int ps = valid ? pu : 0;
+    const int d = valid ? __builtin_amdgcn_readlane(depth_v, ps) + 1 : 0;
+    depth_v = t == u ? d : depth_v;
+    const bool ok = valid && ((okm >> ps) & 1ull) &&
+                    __builtin_amdgcn_readlane(dr, u) == __builtin_amdgcn_readlane(gv, ps);
+    if (ok) {
+      okm |= 1ull << u;
+      if (d > dend) {
+        end = u;
+        dend = d;
+      }
+    }
   }
-  __syncthreads();
+  // Lane i < L: the node at depth i + 1 on the root-to-end path; -1 beyond.
+  int32_t path_v = -1;
+  int u = end;
+  for (int i = dend - 1; i >= 0; --i) {
+    path_v = t == i ? u : path_v;
+    u = __builtin_amdgcn_readlane(par, u);
+  }
   if (t == 0) {
-    ok[0] = 1;
-    depth[0] = 0;
-    int end = 0;
-    for (int u = 1; u < n; ++u) {
-      const int pu = par[u];
-      const bool valid = pu >= 0 && pu < u;
-      ok[u] = valid && ok[pu] && dr[u] == g[pu];
-      depth[u] = valid ? depth[pu] + 1 : 0;
-      if (ok[u] && depth[u] > depth[end]) end = u;
-    }
-    const int L = depth[end];
     result[0] = end;
-    result[1] = L;
-    result[2] = g[end];
-    int u = end;
-    for (int i = L - 1; i >= 0; --i) {
-      result[3 + i] = u;
-      u = par[u];
-    }
-    for (int i = L; i < n; ++i) result[3 + i] = -1;
+    result[1] = dend;
+    result[2] = __builtin_amdgcn_readlane(gv, end);
   }
+  if (t < n) result[3 + t] = path_v;
 }
 
 }  // namespace

@@ -67,7 +67,7 @@ def test_gemm_small_shapes_all_paths(M, K, N):
                         f"M={M} K={K} N={N} path={path} {out_dtype}")
 
 
-# The persistent tiled kernel (K % 1024 == 0, M > 16): 128 x 80 tiles, 256-K steps, scale bytes
+# The persistent tiled kernel (K % 1024 == 0, M > 16): 64 x 160 tiles, 256-K steps, scale bytes
 # fetched four steps at a time, loads three steps ahead across tile boundaries.  Cases: one scale
 # group, ragged M and N, more tiles than workgroups (600 and 262 tiles: several tiles per
 # workgroup, with and without a tile count divisible by 8), a single tile, M just above 16.  K %
