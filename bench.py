@@ -120,6 +120,10 @@ class Pipeline:
 
     def _gemm1(self, i):
         wc, ws, gw = self.l1.copies[i % self.R]
+        if self.dynamic_scale and self.split_ws is None:  # scale, quantization and GEMM in one call
+            B.nvfp4_quantize_gemm_dynamic(self.a, wc, ws, gw, out_dtype=self.out_dtype, out=self.y1,
+                                          a_codes=self.ac1, a_scales=self.as1, g_a=self.g1)
+            return
         if self.dynamic_scale:
             B.nvfp4_act_global_scale(self.a, out=self.g1)
         if self.split_ws is not None:  # quantization, then the GEMM with its K split over workgroups
@@ -332,8 +336,9 @@ def main() -> int:
     ap.add_argument("--workload", default="decode_up", choices=sorted(WL.WORKLOADS) + ["kv_fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dynamic-act-scale", action="store_true",
-                    help="compute the activation scale on the device in every step (nvfp4_act_global_scale) "
-                         "instead of the static calibrated one")
+                    help="compute the activation scale on the device in every step (inside the fused GEMV "
+                         "where the step is one kernel, else nvfp4_act_global_scale) instead of the static "
+                         "calibrated one")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-reference-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (a known-size "
@@ -363,6 +368,7 @@ def main() -> int:
     step_ms = timed_replays(step_graphs, K, P.R) / K
     kern_ms = timed_replays(gemm_graphs, K, P.R) / K
     kname = ("LM head + fused argmax + tree acceptance" if P.tree else
+             "fused scale + quantize + FP4 GEMV" if P.fused_single_kernel and args.dynamic_act_scale else
              "fused quantize + FP4 GEMV" if P.fused_single_kernel else
              "M<=16 weight-streaming GEMM (gemm_m16_kernel)" if 3 <= wl.M <= 16 else
              "first GEMM (its output's NVFP4 form emitted in the epilogue)" if wl.chain and not args.dynamic_act_scale else

@@ -226,6 +226,29 @@ nvfp4_status nvfp4_quantize_gemm(int64_t M, int64_t K, int64_t N,
                                  void* out, nvfp4_dtype out_dt, uint8_t* a_codes, uint8_t* a_scales,
                                  void* stream);
 
+/* nvfp4_quantize_gemm with the activations' tensor scale computed on the
+ * device: the decode step's nvfp4_act_global_scale + nvfp4_quantize_act +
+ * nvfp4_gemm.
+ *   a_global  out: device float, g_a = fl32(amax|A| / 2688) (0 for an all-zero
+ *             or empty A), bit-identical to nvfp4_act_global_scale; it must
+ *             not alias any other argument.
+ *   other arguments as nvfp4_quantize_gemm; a_codes / a_scales are quantized
+ *             with that g_a and out is bit-identical to the three calls.
+ * For M <= 2 with K a multiple of 1024 in [1024, 8192] this is one kernel:
+ * every workgroup reduces the largest magnitude of the rows it already loads
+ * for quantization, so neither the scale launch nor its round trip through
+ * memory remains; workgroup 0 stores g_a.  Other shapes run the scale kernel,
+ * then nvfp4_quantize_gemm's launches.  M == 0 only sets g_a = 0.
+ * Errors as nvfp4_quantize_gemm, a_global always required.
+ * Cites: the page section "Using NVFP4 quantization to accelerate Qwen3.6-27B
+ * inference" (NVFP4 activations; a dynamic per-tensor scale is the alternative
+ * to the calibrated one). */
+nvfp4_status nvfp4_quantize_gemm_dynamic(int64_t M, int64_t K, int64_t N,
+                                         const void* a, nvfp4_dtype a_dt, float* a_global,
+                                         const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                                         void* out, nvfp4_dtype out_dt, uint8_t* a_codes, uint8_t* a_scales,
+                                         void* stream);
+
 /* FP8 E4M3 KV-cache codec: encode.
  *   x      [n] KV values in x_dt (NVFP4_F32 or NVFP4_BF16), device, any layout
  *          (the codec is elementwise).

@@ -25,7 +25,8 @@ PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 EXPORTS = ("nvfp4_abi_version", "nvfp4_act_global_scale", "nvfp4_gemm", "nvfp4_gemm_ex",
            "nvfp4_gemm_quantize_output", "nvfp4_gemm_workspace_bytes", "nvfp4_gemm_ws", "nvfp4_kv_fp8_decode", "nvfp4_kv_fp8_encode",
            "nvfp4_quantize_act",
-           "nvfp4_quantize_gemm", "nvfp4_quantize_weights", "nvfp4_status_string", "nvfp4_tree_accept",
+           "nvfp4_quantize_gemm", "nvfp4_quantize_gemm_dynamic", "nvfp4_quantize_weights", "nvfp4_status_string",
+           "nvfp4_tree_accept",
            "nvfp4_tree_verify")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -55,6 +56,7 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
     lib.nvfp4_gemm_workspace_bytes.restype = i64
     lib.nvfp4_quantize_gemm.argtypes = [i64, i64, i64, p, i32, p, p, p, p, p, i32, p, p, p]
+    lib.nvfp4_quantize_gemm_dynamic.argtypes = [i64, i64, i64, p, i32, p, p, p, p, p, i32, p, p, p]
     lib.nvfp4_tree_accept.argtypes = [i64, p, p, p, p, p]
     lib.nvfp4_kv_fp8_encode.argtypes = [p, i32, i64, p, p, p]
     lib.nvfp4_act_global_scale.argtypes = [p, i32, i64, i64, p, p]
@@ -288,6 +290,48 @@ def nvfp4_quantize_gemm(a: torch.Tensor, g_a: torch.Tensor, w_codes: torch.Tenso
                                       a_scales.data_ptr(), _stream(dev)),
            "nvfp4_quantize_gemm")
     return out, a_codes, a_scales
+
+
+def nvfp4_quantize_gemm_dynamic(a: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, g_w: torch.Tensor,
+                                out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                                a_codes: Optional[torch.Tensor] = None, a_scales: Optional[torch.Tensor] = None,
+                                g_a: Optional[torch.Tensor] = None
+                                ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Raw activations a [M, K] times the NVFP4 weights with the activations' tensor scale
+    computed on the device: returns (out [M, N], a_codes, a_scales, g_a [1])."""
+    if a.dim() != 2 or w_codes.dim() != 2:
+        raise ValueError("a and w_codes must be 2-D")
+    M, K = a.shape
+    N = w_codes.shape[0]
+    if w_codes.shape[1] != K // 2 or w_scales.shape != (N, K // 16):
+        raise ValueError("inconsistent operand shapes")
+    if w_codes.dtype != torch.uint8 or w_scales.dtype != torch.uint8:
+        raise ValueError("codes and scales must be uint8")
+    if g_w.dtype != torch.float32 or g_w.numel() != 1:
+        raise ValueError("tensor scales must be float32 tensors of one element")
+    dev = _dev(a, w_codes, w_scales, g_w)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+    elif out.shape != (M, N) or out.dtype != out_dtype:
+        raise ValueError("out must be [M, N] of out_dtype")
+    if a_codes is None:
+        a_codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    if a_scales is None:
+        a_scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    if g_a is None:
+        g_a = torch.empty((1,), dtype=torch.float32, device=dev)
+    if g_a.dtype != torch.float32 or g_a.numel() != 1:
+        raise ValueError("g_a must be a float32 tensor of one element")
+    if a_codes.dtype != torch.uint8 or a_scales.dtype != torch.uint8 or \
+            a_codes.numel() != M * (K // 2) or a_scales.numel() != M * (K // 16):
+        raise ValueError("a_codes/a_scales must be uint8 of [M, K/2] / [M, K/16] elements")
+    _dev(a, out, a_codes, a_scales, g_a)
+    _check(load().nvfp4_quantize_gemm_dynamic(M, K, N, a.data_ptr(), _dt(a.dtype), g_a.data_ptr(),
+                                              w_codes.data_ptr(), w_scales.data_ptr(), g_w.data_ptr(),
+                                              out.data_ptr(), _dt(out_dtype), a_codes.data_ptr(),
+                                              a_scales.data_ptr(), _stream(dev)),
+           "nvfp4_quantize_gemm_dynamic")
+    return out, a_codes, a_scales, g_a
 
 
 def _int32_vec(t: torch.Tensor, n: int, name: str) -> None:

@@ -41,7 +41,7 @@ const char* nvfp4_status_string(nvfp4_status s) {
   return "unknown status";
 }
 
-int nvfp4_abi_version(void) { return 7; }
+int nvfp4_abi_version(void) { return 8; }
 
 nvfp4_status nvfp4_quantize_weights(const void* w, nvfp4_dtype w_dt, int64_t N, int64_t K,
                                     uint8_t* w_codes, uint8_t* w_scales, float* w_global,
@@ -241,6 +241,50 @@ nvfp4_status nvfp4_quantize_gemm(int64_t M, int64_t K, int64_t N,
     return from_hip(nvfp4::launch_gemv_fp4(g, s));
   }
   hipError_t e = nvfp4::launch_quantize(a, a_dt == NVFP4_BF16, M, K, a_global, a_codes, a_scales, s);
+  if (e != hipSuccess || N == 0) return from_hip(e);
+  return from_hip(M <= 16 ? nvfp4::launch_gemm_skinny(g, s) : nvfp4::launch_gemm_tiled(g, s));
+}
+
+nvfp4_status nvfp4_quantize_gemm_dynamic(int64_t M, int64_t K, int64_t N,
+                                         const void* a, nvfp4_dtype a_dt, float* a_global,
+                                         const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                                         void* out, nvfp4_dtype out_dt, uint8_t* a_codes, uint8_t* a_scales,
+                                         void* stream) {
+  if (!dtype_ok(a_dt) || !dtype_ok(out_dt)) return NVFP4_ERR_DTYPE;
+  if (!shape_ok(M, K) || !shape_ok(N, K)) return NVFP4_ERR_SHAPE;
+  if (M > 0 && N >= kMaxElems / M) return NVFP4_ERR_SHAPE;
+  if ((M <= 16 ? (M + 15) / 16 : (M + 127) / 128) > kMaxGridY) return NVFP4_ERR_SHAPE;
+  if (!a_global) return NVFP4_ERR_NULL;
+  if (!aligned4(a_global)) return NVFP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M == 0) return from_hip(nvfp4::launch_act_global(a, a_dt == NVFP4_BF16, 0, a_global, s));  // g_a = 0
+  if (!a || !a_codes || !a_scales) return NVFP4_ERR_NULL;
+  if (N > 0 && (!w_codes || !w_scales || !w_global || !out)) return NVFP4_ERR_NULL;
+  if (!aligned16(a) || !aligned16(a_codes) || !aligned16(a_scales)) return NVFP4_ERR_ALIGN;
+  if (N > 0 && (!aligned16(w_codes) || !aligned16(w_scales) || !aligned16(out) || !aligned4(w_global)))
+    return NVFP4_ERR_ALIGN;
+  nvfp4::GemmArgs g;
+  g.M = (int)M;
+  g.K = (int)K;
+  g.N = (int)N;
+  g.ac = a_codes;
+  g.as = a_scales;
+  g.ga = a_global;
+  g.wc = w_codes;
+  g.ws = w_scales;
+  g.gw = w_global;
+  g.out = out;
+  g.out_bf16 = out_dt == NVFP4_BF16;
+  if (N > 0 && nvfp4::gemv_fp4_supported(g)) {  // one kernel: scale and quantization in its set-up
+    g.a_raw = a;
+    g.a_raw_bf16 = a_dt == NVFP4_BF16;
+    g.ac_out = a_codes;
+    g.as_out = a_scales;
+    g.ga_dynamic = a_global;
+    return from_hip(nvfp4::launch_gemv_fp4(g, s));
+  }
+  hipError_t e = nvfp4::launch_act_global(a, a_dt == NVFP4_BF16, M * K, a_global, s);
+  if (e == hipSuccess) e = nvfp4::launch_quantize(a, a_dt == NVFP4_BF16, M, K, a_global, a_codes, a_scales, s);
   if (e != hipSuccess || N == 0) return from_hip(e);
   return from_hip(M <= 16 ? nvfp4::launch_gemm_skinny(g, s) : nvfp4::launch_gemm_tiled(g, s));
 }

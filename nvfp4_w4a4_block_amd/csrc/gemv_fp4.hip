@@ -71,6 +71,10 @@ size_t fp4_lds_bytes(int MR, int K, int G) {
 // or 2 (fp32) reads the raw activation rows and quantizes their 16-blocks in
 // the set-up (quantize_block16, bit-identical to the activation quantizer),
 // every workgroup for itself; workgroup 0 also stores the codes and scales.
+// With p.ga_dynamic set, the tensor scale is computed there too: the largest
+// magnitude over the raw rows (each workgroup holds all of them), reduced
+// across the workgroup, g_a = fl32(amax / 2688), as the standalone scale
+// kernel computes it.
 template <int MR, int L, int D, bool OUT_BF16, int FUSE>
 __global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
   static_assert(L % D == 0 && D <= L, "ring depth must divide the line count");
@@ -114,6 +118,7 @@ __global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
   constexpr int kRawPerThread = (kRawBlocks + 255) / 256;
   constexpr int kRawVec = FUSE == 2 ? 4 : 2;  // 16-byte loads per block (fp32 : bf16)
   u4_t xr[FUSE == 0 ? 1 : kRawPerThread][kRawVec];
+  [[maybe_unused]] float ga_used = 0.0f;  // fused: the tensor scale the rows were quantized with
   if constexpr (FUSE == 0) {
 #pragma unroll
     for (int s = 0; s < kFillPerThread; ++s) {
@@ -177,24 +182,52 @@ __global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
       *reinterpret_cast<f4_t*>(asc + 4 * a_dw) = f4_t{lo.x, lo.y, hi.x, hi.y};
     }
   } else {
-    const float ga = *p.ga;
+    // raw value e (0..15) of this thread's block s, as fp32
+    // (The vector element is copied to a scalar before the bit cast: a bit
+    // cast applied to the element expression itself compiled to a read of
+    // the vector's first element.)
+    auto raw = [&](int s, int e) {
+      if constexpr (FUSE == 2) {
+        const uint32_t w = xr[s][e >> 2][e & 3];
+        return __builtin_bit_cast(float, w);
+      } else {  // two bf16 per word: element 2c in the low half
+        const uint32_t w = xr[s][e >> 3][(e >> 1) & 3];
+        return __builtin_bit_cast(float, (e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+      }
+    };
+    float ga;
+    if (p.ga_dynamic != nullptr) {
+      // blocks past the rows were loaded as zeros
+      float m = 0.0f;
+#pragma unroll
+      for (int s = 0; s < kRawPerThread; ++s)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(raw(s, e)));
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+      __shared__ float wave_max[kWaves];
+      if (lane == 0) wave_max[wave] = m;
+      // workgroup barrier for this LDS exchange only: the weight loads stay in flight
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      float b = wave_max[0];
+#pragma unroll
+      for (int i = 1; i < kWaves; ++i) b = __builtin_fmaxf(b, wave_max[i]);
+      ga = b / 2688.0f;
+      if (blockIdx.x == 0 && threadIdx.x == 0) *p.ga_dynamic = ga;
+    } else {
+      ga = *p.ga;
+    }
+    ga_used = ga;
 #pragma unroll
     for (int s = 0; s < kRawPerThread; ++s) {
       const uint32_t b = threadIdx.x + 256u * s;
       if (b < (uint32_t)kRawBlocks) {
         float x[16];
 #pragma unroll
-        for (int v = 0; v < kRawVec; ++v)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint32_t w = xr[s][v][c];
-            if constexpr (FUSE == 2) {
-              x[4 * v + c] = __builtin_bit_cast(float, w);
-            } else {  // two bf16: element 2c in the low half
-              x[8 * v + 2 * c] = __builtin_bit_cast(float, w << 16);
-              x[8 * v + 2 * c + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
-            }
-          }
+        for (int e = 0; e < 16; ++e) x[e] = raw(s, e);
         uint32_t w0, w1;
         const uint32_t sb = quantize_block16(x, ga, w0, w1);
         const uint32_t m = b >= 16u * L ? 1u : 0u;
@@ -299,7 +332,7 @@ __global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
   }
 
   // ---- epilogue: same-wave LDS ops are ordered ----
-  const float gscale = (*p.ga) * (*p.gw);
+  const float gscale = (FUSE == 0 ? *p.ga : ga_used) * (*p.gw);
   for (int idx = lane; idx < G * 8 * MR; idx += 64) {
     const uint32_t n = row0 + (uint32_t)(idx / MR);
     const int m = idx % MR;

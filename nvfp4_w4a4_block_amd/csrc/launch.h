@@ -54,6 +54,10 @@ struct GemmArgs {
   const float* y_global = nullptr;
   uint8_t* y_codes = nullptr;
   uint8_t* y_scales = nullptr;
+  // Fused GEMV only (a_raw set): when ga_dynamic is set the tensor scale is not read from ga:
+  // every workgroup computes g_a = fl32(amax|A| / 2688) from the raw rows it
+  // holds, uses it, and workgroup 0 stores it to *ga_dynamic.
+  float* ga_dynamic = nullptr;
 };
 
 constexpr int kKeySlots = 64;  // argmax key slots per row

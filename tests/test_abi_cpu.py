@@ -42,7 +42,7 @@ def test_status_strings_and_version(lib):
     for s in range(6):
         assert B.status_string(s)
     assert B.status_string(99) == "unknown status"
-    assert lib.nvfp4_abi_version() == 7
+    assert lib.nvfp4_abi_version() == 8
 
 
 def gemm(lib, M, K, N, ptrs=(A16,) * 7, out_dt=B.NVFP4_BF16, path=B.PATH_AUTO):
@@ -173,6 +173,26 @@ def test_quantize_gemm_validation(lib):
         assert qgemm(lib, 1, 5120, 64, ptrs=tuple(ptrs)) == B.NVFP4_ERR_NULL, k
         ptrs[k] = A16 + (2 if k in (1, 4) else 8)  # scalars need 4 bytes, arrays 16
         assert qgemm(lib, 1, 5120, 64, ptrs=tuple(ptrs)) == B.NVFP4_ERR_ALIGN, k
+
+
+def test_quantize_gemm_dynamic_validation(lib):
+    """Same rules as nvfp4_quantize_gemm, with the tensor scale an output that is always
+    required (checked before anything else that could launch)."""
+    def dq(M, K, N, ptrs=(A16,) * 8, a_dt=B.NVFP4_BF16, out_dt=B.NVFP4_BF16):
+        a, ga, wc, wsc, gw, out, ac, asc = ptrs
+        return lib.nvfp4_quantize_gemm_dynamic(M, K, N, a, a_dt, ga, wc, wsc, gw, out, out_dt, ac, asc, None)
+    assert dq(1, 5120, 64, a_dt=7) == B.NVFP4_ERR_DTYPE
+    assert dq(1, 5120, 64, out_dt=2) == B.NVFP4_ERR_DTYPE
+    assert dq(1, 24, 64) == B.NVFP4_ERR_SHAPE
+    assert dq(-1, 32, 64) == B.NVFP4_ERR_SHAPE
+    assert dq(1, 32, -1) == B.NVFP4_ERR_SHAPE
+    assert dq(0, 32, 64, ptrs=(A16, None) + (A16,) * 6) == B.NVFP4_ERR_NULL  # g_a is written even for M == 0
+    for k in range(8):
+        ptrs = [A16] * 8
+        ptrs[k] = None
+        assert dq(1, 5120, 64, ptrs=tuple(ptrs)) == B.NVFP4_ERR_NULL, k
+        ptrs[k] = A16 + (2 if k in (1, 4) else 8)  # scalars need 4 bytes, arrays 16
+        assert dq(1, 5120, 64, ptrs=tuple(ptrs)) == B.NVFP4_ERR_ALIGN, k
 
 
 def test_tree_entry_points_validate(lib):

@@ -64,3 +64,48 @@ def test_decode_step_with_dynamic_scale():
     wp, wsp = Q.quantize_packed(inp.W[cols], g_w)
     C, T = G.gemm_ref(ap, asp, g_a, wp, wsp, g_w)
     U.assert_within(U.host(out)[:, cols], C, T + U.out_rounding_slack(C, torch.bfloat16), "dynamic g_a decode")
+
+
+# nvfp4_quantize_gemm_dynamic: one kernel for M <= 2 with K % 1024 == 0 in [1024, 8192] (every
+# workgroup reduces the rows' largest magnitude itself), otherwise the scale kernel followed by
+# nvfp4_quantize_gemm.  Cases: the fused kernel at decode size (bf16, with outlier channels) and
+# with fp32 rows, two rows, the smallest and largest fused K, an all-zero row, and unfused shapes
+# (K outside the set, three rows).
+DYN_CASES = [(1, 5120, 25600, torch.bfloat16), (1, 5120, 3000, torch.float32), (2, 4096, 1000, torch.bfloat16),
+             (1, 1024, 513, torch.float32), (2, 8192, 700, torch.bfloat16), (1, 2048, 300, "zeros"),
+             (1, 2304, 500, torch.bfloat16), (3, 5120, 800, torch.float32)]
+
+
+@pytest.mark.parametrize("M,K,N,kind", DYN_CASES, ids=lambda v: str(v).replace("torch.", ""))
+def test_quantize_gemm_dynamic_matches_three_calls_and_oracle(M, K, N, kind):
+    rng = np.random.default_rng(M * 7 + K + N)
+    A = (rng.standard_normal((M, K)) * np.exp(rng.uniform(-2, 2))).astype(np.float32)
+    A[:, rng.choice(K, size=max(1, K // 200), replace=False)] *= 20.0  # outlier channels
+    dtype = torch.bfloat16 if kind == "zeros" else kind
+    if kind == "zeros":
+        A[:] = 0.0
+    if dtype == torch.bfloat16:
+        bits = WL.f32_to_bf16_bits(A)
+        a, A_seen = U.dev_bf16_bits(bits), WL.bf16_bits_to_f32(bits)
+    else:
+        a, A_seen = U.dev_f32(A), A
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    wc, ws, gw = B.nvfp4_quantize_weights(U.dev_f32(W))
+    for out_dtype in (torch.bfloat16, torch.float32):
+        out, ac, asc, ga = B.nvfp4_quantize_gemm_dynamic(a, wc, ws, gw, out_dtype=out_dtype)
+        ga3 = B.nvfp4_act_global_scale(a)
+        out3, ac3, asc3 = B.nvfp4_quantize_gemm(a, ga3, wc, ws, gw, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert U.f32_bits(ga.item()) == U.f32_bits(ga3.item())
+        assert torch.equal(ac, ac3) and torch.equal(asc, asc3)
+        assert torch.equal(out.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32),
+                           out3.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32))
+    g_a = Q.global_scale(A_seen)
+    assert U.f32_bits(ga.item()) == U.f32_bits(g_a)
+    ap, asp = Q.quantize_packed(A_seen, g_a)
+    np.testing.assert_array_equal(U.host(ac), ap)
+    np.testing.assert_array_equal(U.host(asc), asp)
+    cols = np.random.default_rng(3).choice(N, size=min(N, 96), replace=False)
+    wp, wsp = Q.quantize_packed(W[cols], Q.global_scale(W))
+    C, T = G.gemm_ref(ap, asp, g_a, wp, wsp, Q.global_scale(W))
+    U.assert_within(U.host(out)[:, cols], C, T, f"M={M} K={K} N={N}")
