@@ -8,7 +8,9 @@
 // fl32(x * inv), code = E4M3 of y rounded to nearest even, saturating at 448,
 // sign bit of y.  Decode: fl32(e4m3(code) * s), as fp32 or rounded to bf16.
 // Both kernels stream: 16 elements per thread per chunk, a few chunks' loads
-// in flight per thread, a guarded tail for n % 16.
+// in flight per thread, a guarded tail for n % 16.  The streams are read once:
+// their loads carry the non-temporal hint (measured 7% faster encode, 12%
+// faster decode; the same hint on the stores made the decode slower).
 #pragma clang fp contract(off)
 #include "device_common.h"
 #include "launch.h"
@@ -41,7 +43,7 @@ template <bool BF16>
 __device__ __forceinline__ void load16(const void* x, int64_t c, float* v) {
   if constexpr (BF16) {
     const u4_t* p = reinterpret_cast<const u4_t*>(x) + 2 * c;
-    const u4_t a = p[0], b = p[1];
+    const u4_t a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = __uint_as_float(a[i] << 16);
@@ -53,7 +55,7 @@ __device__ __forceinline__ void load16(const void* x, int64_t c, float* v) {
     const u4_t* p = reinterpret_cast<const u4_t*>(x) + 4 * c;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const u4_t a = p[j];
+      const u4_t a = __builtin_nontemporal_load(p + j);
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[4 * j + i] = __uint_as_float(a[i]);
     }
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint8_t* q, int64_
     u4_t w[kChunksPerThread];
 #pragma unroll
     for (int u = 0; u < kChunksPerThread; ++u)
-      if (c0 + u * T < chunks) w[u] = reinterpret_cast<const u4_t*>(q)[c0 + u * T];
+      if (c0 + u * T < chunks) w[u] = __builtin_nontemporal_load(reinterpret_cast<const u4_t*>(q) + c0 + u * T);
 #pragma unroll
     for (int u = 0; u < kChunksPerThread; ++u) {
       if (c0 + u * T < chunks) {
