@@ -548,10 +548,12 @@ static_assert(kSbLds + 1024 <= kSbMaxLds, "SB LDS budget");
 // scales for all its lines staged once (SB), two pairs of lines in flight,
 // cached loads.  K
 // is split over workgroups when the rows alone give fewer than ~4 waves per
-// CU (about 34 lines, 4352 K-elements, per split measured best) or when the
-// staged activations would not fit the LDS.  NVFP4_M16_{G,RB,KS,KZ,D,CP}
-// NVFP4_M16_AW and NVFP4_M16_SB override the choice (tuning knobs; results
-// change only by fp32 summation order).
+// CU (up to about 7.5 waves per CU in all, at least 6 lines per split; below)
+// or when the staged activations would not fit the LDS.
+// NVFP4_M16_{G,RB,KS,KZ,D,CP}, NVFP4_M16_AW and NVFP4_M16_SB override the
+// choice (tuning knobs; results change only by fp32 summation order).
+// Without a workspace, a starved product with a long K goes to the skinny
+// kernel instead (gemm_m16_preferred): more than twice this many lines.
 constexpr int kSplitLines = 34;
 
 Plan make_plan(const GemmArgs& a, bool can_split) {
