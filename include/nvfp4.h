@@ -149,8 +149,9 @@ nvfp4_status nvfp4_gemm_ex(int64_t M, int64_t K, int64_t N,
 
 /* Size in bytes of the workspace with which nvfp4_gemm_ws splits the
  * contraction of an (M, K, N) product over several workgroups; 0 when it
- * would not (M outside 3..16, K not a multiple of 128, or enough rows to fill
- * the GPU without a split).  Depends only on (M, K, N) and the device's
+ * would not (M outside 3..16, K not a multiple of 128, a short K (a multiple
+ * of 256 up to 8192) with N <= 16384, which a kernel without a split serves
+ * faster, or enough rows to fill the GPU without a split).  Depends only on (M, K, N) and the device's
  * compute-unit count.  At the tree-verification pass of a down-projection
  * (M = 16, K = 25600, N = 5120) it is a few MiB.
  * Cites: the section on tree-based multi-token prediction (one pass over the

@@ -151,6 +151,7 @@ int64_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   g.M = (int)M;
   g.K = (int)K;
   g.N = (int)N;
+  if (nvfp4::gemm_m16_small_prefers_skinny(g)) return 0;  // runs the skinny kernel, unsplit
   return nvfp4::gemm_m16_workspace_bytes(g);
 }
 

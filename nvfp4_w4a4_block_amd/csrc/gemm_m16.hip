@@ -687,8 +687,20 @@ bool gemm_m16_supported(const GemmArgs& a) {
 // workgroups as CUs and more than two splits' worth of lines: the tree-
 // verification down-projection, 5120 x 25600, runs 67 us unsplit here against
 // 31 us in the older skinny kernel and 21 us split).
+// Short K (up to 8192, a multiple of 256) and at most 16384 rows: the skinny
+// kernel, with fewer dependent memory round trips per wave, is faster than
+// this one even split (same-process measurements at M = 16: K = 5120 and N =
+// 1024 / 5120 / 8192 / 16384 12-19% / 16% / 19% / 4% faster, K = 2560 30%,
+// K = 8192 4%; at N = 25600, K = 12288 or K = 25600 this kernel is 25-48%
+// faster).  NVFP4_M16_SMALL=0 turns the rule off.
+bool gemm_m16_small_prefers_skinny(const GemmArgs& a) {
+  return a.M >= 3 && a.M <= 16 && a.K <= 8192 && a.K % 256 == 0 && a.N <= 16384 &&
+         env_int("NVFP4_M16_SMALL", 1) == 1;
+}
+
 bool gemm_m16_preferred(const GemmArgs& a) {
   if (!gemm_m16_supported(a)) return false;
+  if (gemm_m16_small_prefers_skinny(a)) return false;
   const bool split = have_workspace(a) && a.workspace_bytes >= gemm_m16_workspace_bytes(a);
   if (split) return true;
   const Plan pl = make_plan(a, false);

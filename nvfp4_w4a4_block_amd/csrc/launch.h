@@ -86,6 +86,7 @@ hipError_t launch_gemv_fp4(const GemmArgs& a, hipStream_t stream);
 // a workspace K <= 7168).  gemm_m16_workspace_bytes() is the workspace that
 // lets it split K over workgroups (0 when it would not).
 bool gemm_m16_supported(const GemmArgs& a);
+bool gemm_m16_small_prefers_skinny(const GemmArgs& a);  // the skinny kernel serves this product instead
 bool gemm_m16_preferred(const GemmArgs& a);  // supported, and not starved of workgroups unsplit
 int64_t gemm_m16_workspace_bytes(const GemmArgs& a);
 hipError_t launch_gemm_m16(const GemmArgs& a, hipStream_t stream);

@@ -112,7 +112,7 @@ def test_gemm_quantize_output_validation(lib):
 def test_gemm_workspace_bytes_host_cases(lib):
     """Shapes the split path never takes need no workspace (decided on the host, no HIP call):
     one or two rows (the GEMV), more than 16 rows (the tiled path), K not a multiple of 128,
-    invalid shapes."""
+    short-K products with N <= 16384 (the skinny kernel), invalid shapes."""
     f = lib.nvfp4_gemm_workspace_bytes
     assert f(1, 25600, 5120) == 0
     assert f(2, 25600, 5120) == 0
@@ -122,6 +122,9 @@ def test_gemm_workspace_bytes_host_cases(lib):
     assert f(16, 25600, 0) == 0
     assert f(16, 24, 5120) == 0
     assert f(-1, 256, 64) == 0
+    assert f(16, 5120, 5120) == 0  # short K, N <= 16384: the skinny kernel, unsplit
+    assert f(16, 8192, 16384) == 0
+    assert f(16, 25600, 5120) > 0  # the tree-verification down-projection splits K
 
 
 def test_empty_gemm_is_ok_without_pointers(lib):

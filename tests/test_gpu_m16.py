@@ -23,7 +23,7 @@ from oracle import quant as Q
 pytestmark = pytest.mark.gpu
 
 KNOBS = ("NVFP4_M16_G", "NVFP4_M16_RB", "NVFP4_M16_KS", "NVFP4_M16_KZ", "NVFP4_M16_D", "NVFP4_M16_CP",
-         "NVFP4_M16_AW", "NVFP4_M16_SB")
+         "NVFP4_M16_AW", "NVFP4_M16_SB", "NVFP4_M16_SMALL")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -66,8 +66,12 @@ CASES = [(3, 128, 1), (5, 384, 37), (16, 1024, 300), (7, 2688, 129), (16, 6272, 
          (16, 9216, 1000), (11, 25600, 300), (16, 5120, 3000), (4, 640, 2049)]
 
 
+@pytest.mark.parametrize("small", [1, 0], ids=["dispatch", "m16-forced"])
 @pytest.mark.parametrize("M,K,N", CASES)
-def test_m16_with_and_without_workspace(M, K, N):
+def test_m16_with_and_without_workspace(M, K, N, small, knobs):
+    """small=1: the library's dispatch (short-K products with N <= 16384 run the skinny kernel);
+    small=0: the M-tile kernel for every shape it supports."""
+    knobs(SMALL=small)
     dev, C, T = _pair(M, K, N, 11 * M + K + N)
     for i, ws in enumerate((None, "auto")):
         out_dtype = torch.float32 if i == 0 else torch.bfloat16
@@ -90,7 +94,7 @@ PLANS = [dict(G=1, RB=1, KS=1, KZ=1, D=1), dict(G=4, RB=2, KS=4, KZ=1, D=2), dic
 @pytest.mark.parametrize("plan", PLANS, ids=lambda p: "-".join(f"{k}{v}" for k, v in p.items()))
 @pytest.mark.parametrize("M,K,N", [(16, 5120, 700), (9, 3456, 333)])
 def test_m16_forced_plans(M, K, N, plan, knobs):
-    knobs(**plan)
+    knobs(SMALL=0, **plan)
     dev, C, T = _pair(M, K, N, 3 * M + K + N)
     out = B.nvfp4_gemm(*dev, out_dtype=torch.float32, workspace="auto")
     U.assert_within(U.host(out), C, T, f"M={M} K={K} N={N} plan={plan}")
