@@ -81,11 +81,26 @@ typedef enum {
   NVFP4_BF16 = 1   /* bfloat16, rounded to nearest even when written  */
 } nvfp4_dtype;
 
-/* Path selector for nvfp4_gemm_ex. */
+/* Path selector for nvfp4_gemm_ex.  The first three are the library's
+ * automatic choices; the kernel selectors run one named kernel and return
+ * NVFP4_ERR_SHAPE when that kernel does not take the product.  They exist so
+ * that every kernel can be checked against the others and against a
+ * reference; the result contract is the same for all of them. */
 typedef enum {
-  NVFP4_PATH_AUTO = 0,    /* M <= 16: skinny path; otherwise the tiled path   */
-  NVFP4_PATH_SKINNY = 1,  /* weight-streaming path, any M (tiles M by 16)     */
-  NVFP4_PATH_TILED = 2    /* LDS-tiled MFMA path, any M                       */
+  NVFP4_PATH_AUTO = 0,    /* M <= 16: skinny path; otherwise the tiled path       */
+  NVFP4_PATH_SKINNY = 1,  /* weight-streaming path, any M (tiles M by 16)         */
+  NVFP4_PATH_TILED = 2,   /* LDS-tiled MFMA path, any M                           */
+  NVFP4_KERNEL_GEMV_FP4 = 3,          /* FP4 matrix-core GEMV: M <= 2, K % 1024 == 0,
+                                         1024 <= K <= 8192                        */
+  NVFP4_KERNEL_GEMV_FLAT = 4,         /* memory-order GEMV: M <= 2, K % 256 == 0,
+                                         K >= 2048 (within its LDS budget)        */
+  NVFP4_KERNEL_M16 = 5,               /* M-tile weight stream on f16 matrix cores:
+                                         M <= 16, K % 128 == 0 (never split here) */
+  NVFP4_KERNEL_SKINNY256 = 6,         /* skinny kernel, K % 256 == 0, any M       */
+  NVFP4_KERNEL_SKINNY16 = 7,          /* skinny kernel, any K, any M              */
+  NVFP4_KERNEL_TILED_PERSISTENT = 8,  /* persistent 64x160-tile MFMA kernel,
+                                         K % 1024 == 0                            */
+  NVFP4_KERNEL_TILED = 9              /* 128x128-tile MFMA kernel, any shape      */
 } nvfp4_path;
 
 /* Offline weight quantization (post-training, done once).
@@ -140,19 +155,29 @@ nvfp4_status nvfp4_gemm(int64_t M, int64_t K, int64_t N,
                         const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
                         void* out, nvfp4_dtype out_dt, void* stream);
 
-/* nvfp4_gemm with an explicit path (nvfp4_path); same arguments and result
- * contract.  Exists so that the two paths can be checked against each other. */
+/* nvfp4_gemm with an explicit path or kernel (nvfp4_path); same arguments
+ * and result contract.  An unknown selector -> NVFP4_ERR_DTYPE; a kernel
+ * selector whose kernel does not take (M, K, N) -> NVFP4_ERR_SHAPE. */
 nvfp4_status nvfp4_gemm_ex(int64_t M, int64_t K, int64_t N,
                            const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
                            const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
                            void* out, nvfp4_dtype out_dt, int path, void* stream);
 
+/* The kernel (an NVFP4_KERNEL_* value of nvfp4_path) that nvfp4_gemm_ws runs
+ * for an (M, K, N) product with a workspace of workspace_bytes bytes (0:
+ * nvfp4_gemm), or 0 for an empty or invalid product.  A pure function of its
+ * arguments and the device's compute-unit count; enqueues nothing.
+ * Cites: the page sections on NVFP4 quantization (M = 1 decode), tree-based
+ * multi-token prediction (M = 16) and KV-cache reuse (suffix prefill). */
+int nvfp4_gemm_dispatch(int64_t M, int64_t K, int64_t N, int64_t workspace_bytes);
+
 /* Size in bytes of the workspace with which nvfp4_gemm_ws splits the
  * contraction of an (M, K, N) product over several workgroups; 0 when it
  * would not (M outside 3..16, K not a multiple of 128, a short K (a multiple
  * of 256 up to 8192) with N <= 16384, which a kernel without a split serves
- * faster, or enough rows to fill the GPU without a split).  Depends only on (M, K, N) and the device's
- * compute-unit count.  At the tree-verification pass of a down-projection
+ * faster, or enough rows to fill the GPU without a split).  Depends only on
+ * (M, K, N) and the current device's compute-unit count (one HIP attribute
+ * query; nothing is enqueued).  At the tree-verification pass of a down-projection
  * (M = 16, K = 25600, N = 5120) it is a few MiB.
  * Cites: the section on tree-based multi-token prediction (one pass over the
  * 16 candidates: few output rows, a long contraction). */
@@ -290,9 +315,9 @@ nvfp4_status nvfp4_tree_accept(int64_t n_nodes, const int32_t* parent, const int
  *   M        1..16 tree nodes (rows); K, N (vocabulary): as nvfp4_gemm, with the
  *            nodes' NVFP4 activations a_* and the LM-head weights w_*.
  *   parent, draft: as nvfp4_tree_accept.
- *   logits   optional out [M][N] fp32 (may be NULL when K % 128 == 0 and
- *            K <= 6272: the argmax is then fused into the GEMM and the logits
- *            are not written; other K need it).
+ *   logits   optional out [M][N] fp32 (may be NULL when K % 128 == 0: the
+ *            argmax is then fused into the GEMM and the logits are not
+ *            written; other K need it).
  *   greedy   out [M] int32: each row's argmax (lowest column on ties; -0.0
  *            orders just below +0.0).
  *   result   out [3 + M] int32: as nvfp4_tree_accept.
@@ -310,6 +335,23 @@ nvfp4_status nvfp4_tree_verify(int64_t M, int64_t K, int64_t N,
                                const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
                                const int32_t* parent, const int32_t* draft, float* logits, int32_t* greedy,
                                int32_t* result, uint64_t* keys, void* stream);
+
+/* Read-only streaming ceiling: reads the a_bytes bytes at a and the b_bytes
+ * bytes at b once (16-byte loads, each wave a contiguous span, the loads
+ * marked non-temporal); every lane folds the four words of each of its loads
+ * by XOR and writes sink[0] = its fold only if that equals magic.  Run over the codes and scales of a weight matrix it
+ * measures how fast plain HIP code reads exactly the bytes a GEMV or M = 16
+ * GEMM of that matrix must read: the ceiling those products are reported
+ * against, beside the 8 TB/s of the HBM specification.
+ *   a, b     device arrays, 16-byte aligned (either may be NULL when its size
+ *            is 0); a_bytes, b_bytes multiples of 16 below 2^31.
+ *   sink     device uint32, 4-byte aligned (not written in practice).
+ * Errors: a size out of range -> NVFP4_ERR_SHAPE; a NULL array with a size or
+ * a NULL sink -> NVFP4_ERR_NULL; misaligned -> NVFP4_ERR_ALIGN.
+ * Cites: the page section "Using NVFP4 quantization to accelerate Qwen3.6-27B
+ * inference" (low-batch decoding is bound by DRAM bandwidth). */
+nvfp4_status nvfp4_stream_read(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes, uint32_t* sink,
+                               uint32_t magic, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* nvfp4_status_string(nvfp4_status s);

@@ -21,11 +21,18 @@ LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
 NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_DTYPE, NVFP4_ERR_HIP = range(6)
 NVFP4_F32, NVFP4_BF16 = 0, 1
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
+# kernel selectors of nvfp4_gemm_ex (and values of nvfp4_gemm_dispatch)
+(KERNEL_GEMV_FP4, KERNEL_GEMV_FLAT, KERNEL_M16, KERNEL_SKINNY256, KERNEL_SKINNY16,
+ KERNEL_TILED_PERSISTENT, KERNEL_TILED) = range(3, 10)
+KERNEL_NAMES = {KERNEL_GEMV_FP4: "gemv_fp4_kernel", KERNEL_GEMV_FLAT: "gemv_flat_kernel", KERNEL_M16: "gemm_m16_kernel",
+                KERNEL_SKINNY256: "gemm_skinny256_kernel", KERNEL_SKINNY16: "gemm_skinny_kernel",
+                KERNEL_TILED_PERSISTENT: "gemm_wg_tiled_kernel", KERNEL_TILED: "gemm_tiled_kernel"}
 
-EXPORTS = ("nvfp4_abi_version", "nvfp4_act_global_scale", "nvfp4_gemm", "nvfp4_gemm_ex",
+EXPORTS = ("nvfp4_abi_version", "nvfp4_act_global_scale", "nvfp4_gemm", "nvfp4_gemm_dispatch", "nvfp4_gemm_ex",
            "nvfp4_gemm_quantize_output", "nvfp4_gemm_workspace_bytes", "nvfp4_gemm_ws", "nvfp4_kv_fp8_decode", "nvfp4_kv_fp8_encode",
            "nvfp4_quantize_act",
            "nvfp4_quantize_gemm", "nvfp4_quantize_gemm_dynamic", "nvfp4_quantize_weights", "nvfp4_status_string",
+           "nvfp4_stream_read",
            "nvfp4_tree_accept",
            "nvfp4_tree_verify")
 
@@ -55,6 +62,9 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_gemm_quantize_output.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, p, p, p, p]
     lib.nvfp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
     lib.nvfp4_gemm_workspace_bytes.restype = i64
+    lib.nvfp4_gemm_dispatch.argtypes = [i64, i64, i64, i64]
+    lib.nvfp4_stream_read.argtypes = [p, i64, p, i64, p, ctypes.c_uint32, p]
+    lib.nvfp4_gemm_dispatch.restype = i32
     lib.nvfp4_quantize_gemm.argtypes = [i64, i64, i64, p, i32, p, p, p, p, p, i32, p, p, p]
     lib.nvfp4_quantize_gemm_dynamic.argtypes = [i64, i64, i64, p, i32, p, p, p, p, p, i32, p, p, p]
     lib.nvfp4_tree_accept.argtypes = [i64, p, p, p, p, p]
@@ -65,7 +75,7 @@ def load() -> ctypes.CDLL:
     for f in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_gemm_ws",
               "nvfp4_gemm_quantize_output",
               "nvfp4_quantize_gemm", "nvfp4_tree_accept", "nvfp4_tree_verify", "nvfp4_kv_fp8_encode",
-              "nvfp4_kv_fp8_decode", "nvfp4_act_global_scale"):
+              "nvfp4_kv_fp8_decode", "nvfp4_act_global_scale", "nvfp4_stream_read"):
         getattr(lib, f).restype = i32
     lib.nvfp4_status_string.argtypes = [i32]
     lib.nvfp4_status_string.restype = ctypes.c_char_p
@@ -159,6 +169,12 @@ def gemm_workspace(M: int, K: int, N: int, dev: torch.device) -> Optional[torch.
     if ws is None or ws.numel() < need:
         ws = _gemm_workspaces[dev] = torch.zeros((need,), dtype=torch.uint8, device=dev)
     return ws
+
+
+def gemm_dispatch(M: int, K: int, N: int, workspace_bytes: int = 0) -> int:
+    """The kernel selector (KERNEL_*) the automatic path runs for an (M, K, N) product with a
+    workspace of that size (nvfp4_gemm_dispatch); 0 for an empty or invalid product."""
+    return int(load().nvfp4_gemm_dispatch(M, K, N, workspace_bytes))
 
 
 def nvfp4_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, g_a: torch.Tensor,
@@ -443,3 +459,18 @@ def nvfp4_act_global_scale(a: torch.Tensor, out: Optional[torch.Tensor] = None) 
     _check(load().nvfp4_act_global_scale(a.data_ptr(), _dt(a.dtype), M, K, out.data_ptr(), _stream(dev)),
            "nvfp4_act_global_scale")
     return out
+
+
+def nvfp4_stream_read(a: torch.Tensor, b: torch.Tensor, sink: Optional[torch.Tensor] = None,
+                      magic: int = 0x9E3779B9) -> torch.Tensor:
+    """Reads every byte of a and b once (the read-only streaming ceiling of nvfp4_stream_read);
+    returns the sink (int32 [1] on the device, written only by a lane whose XOR fold of the words
+    it read equals `magic`)."""
+    dev = _dev(a, b)
+    if sink is None:
+        sink = torch.zeros((1,), dtype=torch.int32, device=dev)
+    _dev(a, sink)
+    _check(load().nvfp4_stream_read(a.data_ptr(), a.numel() * a.element_size(), b.data_ptr(),
+                                    b.numel() * b.element_size(), sink.data_ptr(), magic, _stream(dev)),
+           "nvfp4_stream_read")
+    return sink

@@ -31,6 +31,7 @@ SOURCES = {
     "tree.hip": [],
     "kv_fp8.hip": [],
     "gemm_tiled.hip": [],
+    "stream.hip": [],
     "abi.cpp": [],
 }
 

@@ -41,7 +41,7 @@ const char* nvfp4_status_string(nvfp4_status s) {
   return "unknown status";
 }
 
-int nvfp4_abi_version(void) { return 8; }
+int nvfp4_abi_version(void) { return 9; }
 
 nvfp4_status nvfp4_quantize_weights(const void* w, nvfp4_dtype w_dt, int64_t N, int64_t K,
                                     uint8_t* w_codes, uint8_t* w_scales, float* w_global,
@@ -91,21 +91,58 @@ nvfp4_status nvfp4_quantize_act(const void* a, nvfp4_dtype a_dt, int64_t M, int6
 
 namespace {
 
-// nvfp4_gemm_ex / nvfp4_gemm_ws: validation, then the chosen path.
-nvfp4_status gemm_impl(int64_t M, int64_t K, int64_t N,
-                       const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
-                       const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
-                       void* out, nvfp4_dtype out_dt, int path, void* workspace, int64_t workspace_bytes,
-                       void* stream) {
+bool path_ok(int path) { return path >= NVFP4_PATH_AUTO && path <= NVFP4_KERNEL_TILED; }
+
+// Grid rows a path launches for M activation rows (grid.y is at most 65535).
+int64_t grid_rows(int path, int64_t M) {
+  const bool tiled = path == NVFP4_PATH_TILED || path == NVFP4_KERNEL_TILED_PERSISTENT || path == NVFP4_KERNEL_TILED;
+  return tiled ? (M + 127) / 128 : (M + 15) / 16;
+}
+
+// Whether an explicitly selected kernel takes the product.
+bool kernel_takes(int k, const nvfp4::GemmArgs& g) {
+  switch (k) {
+    case NVFP4_KERNEL_GEMV_FP4: return nvfp4::gemv_fp4_supported(g);
+    case NVFP4_KERNEL_GEMV_FLAT: return nvfp4::gemv_flat_supported(g);
+    case NVFP4_KERNEL_M16: return nvfp4::gemm_m16_supported(g);
+    case NVFP4_KERNEL_SKINNY256: return g.K % 256 == 0;
+    case NVFP4_KERNEL_TILED_PERSISTENT: return nvfp4::gemm_tiled_persistent_supported(g);
+    default: return true;  // the skinny16 and simple tiled kernels take any shape
+  }
+}
+
+hipError_t launch_path(int path, const nvfp4::GemmArgs& g, hipStream_t s) {
+  switch (path) {
+    case NVFP4_PATH_SKINNY: return nvfp4::launch_gemm_skinny(g, s);
+    case NVFP4_PATH_TILED: return nvfp4::launch_gemm_tiled(g, s);
+    case NVFP4_KERNEL_GEMV_FP4: return nvfp4::launch_gemv_fp4(g, s);
+    case NVFP4_KERNEL_GEMV_FLAT: return nvfp4::launch_gemv_flat(g, s);
+    case NVFP4_KERNEL_M16: return nvfp4::launch_gemm_m16(g, s);
+    case NVFP4_KERNEL_SKINNY256: return nvfp4::launch_gemm_skinny256(g, s);
+    case NVFP4_KERNEL_SKINNY16: return nvfp4::launch_gemm_skinny16(g, s);
+    case NVFP4_KERNEL_TILED_PERSISTENT: return nvfp4::launch_gemm_tiled_persistent(g, s);
+    default: return nvfp4::launch_gemm_tiled_simple(g, s);
+  }
+}
+
+// Validation of nvfp4_gemm_ex / nvfp4_gemm_ws; on success
+// *path is the resolved path or kernel and *g the arguments (g->M == 0 or
+// g->N == 0: nothing to run).
+nvfp4_status gemm_validate(int64_t M, int64_t K, int64_t N,
+                           const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                           void* out, nvfp4_dtype out_dt, int* path, void* workspace, int64_t workspace_bytes,
+                           nvfp4::GemmArgs* g) {
   if (!dtype_ok(out_dt)) return NVFP4_ERR_DTYPE;
-  if (path != NVFP4_PATH_AUTO && path != NVFP4_PATH_SKINNY && path != NVFP4_PATH_TILED)
-    return NVFP4_ERR_DTYPE;
+  if (!path_ok(*path)) return NVFP4_ERR_DTYPE;
   if (!shape_ok(M, K) || !shape_ok(N, K)) return NVFP4_ERR_SHAPE;
   if (M > 0 && N >= kMaxElems / M) return NVFP4_ERR_SHAPE;
   if (workspace_bytes < 0) return NVFP4_ERR_SHAPE;
-  if (path == NVFP4_PATH_AUTO) path = M <= 16 ? NVFP4_PATH_SKINNY : NVFP4_PATH_TILED;
-  if ((path == NVFP4_PATH_SKINNY ? (M + 15) / 16 : (M + 127) / 128) > kMaxGridY)
-    return NVFP4_ERR_SHAPE;
+  if (*path == NVFP4_PATH_AUTO) *path = M <= 16 ? NVFP4_PATH_SKINNY : NVFP4_PATH_TILED;
+  if (grid_rows(*path, M) > kMaxGridY) return NVFP4_ERR_SHAPE;
+  g->M = (int)M;
+  g->K = (int)K;
+  g->N = (int)N;
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!a_codes || !a_scales || !a_global || !w_codes || !w_scales || !w_global || !out)
     return NVFP4_ERR_NULL;
@@ -114,23 +151,31 @@ nvfp4_status gemm_impl(int64_t M, int64_t K, int64_t N,
       !aligned16(w_scales) || !aligned16(out) || !aligned4(a_global) || !aligned4(w_global) ||
       (workspace && !aligned16(workspace)))
     return NVFP4_ERR_ALIGN;
+  g->ac = a_codes;
+  g->as = a_scales;
+  g->ga = a_global;
+  g->wc = w_codes;
+  g->ws = w_scales;
+  g->gw = w_global;
+  g->out = out;
+  g->out_bf16 = out_dt == NVFP4_BF16;
+  g->workspace = workspace_bytes > 0 ? workspace : nullptr;
+  g->workspace_bytes = workspace_bytes;
+  if (*path >= NVFP4_KERNEL_GEMV_FP4 && !kernel_takes(*path, *g)) return NVFP4_ERR_SHAPE;
+  return NVFP4_OK;
+}
+
+// nvfp4_gemm_ex / nvfp4_gemm_ws: validation, then the chosen path or kernel.
+nvfp4_status gemm_impl(int64_t M, int64_t K, int64_t N,
+                       const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                       void* out, nvfp4_dtype out_dt, int path, void* workspace, int64_t workspace_bytes,
+                       void* stream) {
   nvfp4::GemmArgs g;
-  g.M = (int)M;
-  g.K = (int)K;
-  g.N = (int)N;
-  g.ac = a_codes;
-  g.as = a_scales;
-  g.ga = a_global;
-  g.wc = w_codes;
-  g.ws = w_scales;
-  g.gw = w_global;
-  g.out = out;
-  g.out_bf16 = out_dt == NVFP4_BF16;
-  g.workspace = workspace_bytes > 0 ? workspace : nullptr;
-  g.workspace_bytes = workspace_bytes;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  return from_hip(path == NVFP4_PATH_SKINNY ? nvfp4::launch_gemm_skinny(g, s)
-                                            : nvfp4::launch_gemm_tiled(g, s));
+  const nvfp4_status st = gemm_validate(M, K, N, a_codes, a_scales, a_global, w_codes, w_scales, w_global, out,
+                                        out_dt, &path, workspace, workspace_bytes, &g);
+  if (st != NVFP4_OK || g.M == 0 || g.N == 0) return st;
+  return from_hip(launch_path(path, g, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -153,6 +198,18 @@ int64_t nvfp4_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   g.N = (int)N;
   if (nvfp4::gemm_m16_small_prefers_skinny(g)) return 0;  // runs the skinny kernel, unsplit
   return nvfp4::gemm_m16_workspace_bytes(g);
+}
+
+int nvfp4_gemm_dispatch(int64_t M, int64_t K, int64_t N, int64_t workspace_bytes) {
+  if (M < 1 || N < 1 || !shape_ok(M, K) || !shape_ok(N, K) || N >= kMaxElems / M || workspace_bytes < 0) return 0;
+  nvfp4::GemmArgs g;
+  g.M = (int)M;
+  g.K = (int)K;
+  g.N = (int)N;
+  g.workspace = workspace_bytes > 0 ? &g : nullptr;  // only its presence and size matter here
+  g.workspace_bytes = workspace_bytes;
+  if (M > 16) return nvfp4::gemm_tiled_persistent_supported(g) ? NVFP4_KERNEL_TILED_PERSISTENT : NVFP4_KERNEL_TILED;
+  return nvfp4::skinny_kernel_choice(g);
 }
 
 nvfp4_status nvfp4_gemm_ws(int64_t M, int64_t K, int64_t N,
@@ -357,6 +414,16 @@ nvfp4_status nvfp4_tree_verify(int64_t M, int64_t K, int64_t N,
   }
   if (e != hipSuccess) return from_hip(e);
   return from_hip(nvfp4::launch_tree_accept((int)M, parent, draft, nullptr, keys, greedy, result, s));
+}
+
+nvfp4_status nvfp4_stream_read(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes, uint32_t* sink,
+                               uint32_t magic, void* stream) {
+  if (a_bytes < 0 || b_bytes < 0 || a_bytes >= kMaxElems || b_bytes >= kMaxElems || a_bytes % 16 || b_bytes % 16)
+    return NVFP4_ERR_SHAPE;
+  if (!sink || (a_bytes > 0 && !a) || (b_bytes > 0 && !b)) return NVFP4_ERR_NULL;
+  if (!aligned4(sink) || (a_bytes > 0 && !aligned16(a)) || (b_bytes > 0 && !aligned16(b))) return NVFP4_ERR_ALIGN;
+  return from_hip(nvfp4::launch_read_stream(static_cast<const uint8_t*>(a), a_bytes, static_cast<const uint8_t*>(b),
+                                            b_bytes, sink, magic, static_cast<hipStream_t>(stream)));
 }
 
 nvfp4_status nvfp4_gemm(int64_t M, int64_t K, int64_t N,

@@ -33,18 +33,11 @@
 // bits in [2^-10, 2688]).  The MFMA products are therefore exact and only the
 // fp32 accumulation rounds.  The tensor scales g_a * g_w are applied once in
 // the epilogue.
-#include <stdlib.h>
-
 #include "device_common.h"
 #include "launch.h"
 
 namespace nvfp4 {
 namespace {
-
-int env_int(const char* name, int dflt) {
-  const char* s = getenv(name);
-  return (s && *s) ? atoi(s) : dflt;
-}
 
 constexpr int kMaxWavesK = 8;
 constexpr uint32_t kOOB = 0x80000000u;  // an offset past every buffer (buffers are < 2^31 bytes)
@@ -427,190 +420,6 @@ __global__ __launch_bounds__(64 * kMaxWavesK) void gemm_skinny256_kernel(GemmArg
 }
 
 // ---------------------------------------------------------------------------
-// VALU GEMV for M <= 2 and K % 512 == 0 (single-stream decode).  With one or
-// two activation rows the MFMA's 16-row operand would be mostly padding and,
-// worse, its lane layout limits a load instruction to 64 bytes per weight row.
-// Here the lane layout is free: 16 lanes share a weight row and read 256
-// contiguous bytes (512 codes) of it per instruction, 4 rows per instruction,
-// and each lane reads the 2 scale bytes of its 32 codes (32 contiguous bytes
-// per row).
-//
-// The workgroup first dequantizes the activation rows once into LDS as f16
-// (a = e2m1 * s_a, exact) and every wave reads its 32 values per segment from
-// there.  A wave owns 4*G weight rows over the whole of K and streams its
-// (segment) units through a ring of D units of loads, so memory and
-// arithmetic overlap for the wave's whole life and no partial sums cross
-// waves.  Arithmetic: each weight byte becomes an f16 pair (exact), v_dot2
-// f16 -> fp32 accumulates 8 pairs per 16-block, the block's weight scale is
-// applied with one fp32 FMA, and the 16 lanes of a row are summed at the end
-// in a fixed order; g_a * g_w in the epilogue.
-// ---------------------------------------------------------------------------
-template <int G>
-struct GUnit {
-  u4_t c[G];
-};
-
-template <int MR, int G, int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void gemv_valu_kernel(GemmArgs p) {
-  extern __shared__ __attribute__((aligned(16))) h2_t a_pairs[];  // [MR][K/2]
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane & 15, rr = lane >> 4;
-  const int M = p.M, K = p.K, N = p.N;
-  const uint32_t cstride = (uint32_t)K >> 1, sstride = (uint32_t)K >> 4;
-  const int segs = K >> 9;
-  const int n0 = (blockIdx.x * (blockDim.x >> 6) + wave) * (4 * G);
-
-  const __amdgpu_buffer_rsrc_t ac = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.ac), (short)0, (int)((uint32_t)M * cstride), 0x00020000);
-  const __amdgpu_buffer_rsrc_t as = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.as), (short)0, (int)((uint32_t)M * sstride), 0x00020000);
-  const __amdgpu_buffer_rsrc_t wc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.wc), (short)0, (int)((uint32_t)N * cstride), 0x00020000);
-  const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.ws), (short)0, (int)((uint32_t)N * sstride), 0x00020000);
-
-  // Rows past N lie past the end of the weight buffers and read as zeros.
-  auto load_unit = [&](int seg) {
-    GUnit<G> u;
-    const bool ok = seg < segs;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint32_t row = (uint32_t)(n0 + 4 * g + rr);
-      u.c[g] = __builtin_amdgcn_raw_buffer_load_b128(wc, ok ? row * cstride + (uint32_t)seg * 256 + 16 * c : kOOB, 0, 0);
-    }
-    return u;
-  };
-
-  // Weight loads first (the long latency), then the activation fill.
-  GUnit<G> ring[D];
-#pragma unroll
-  for (int j = 0; j < D; ++j) {
-    ring[j] = load_unit(j);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // The wave's rows are consecutive, so their scale bytes are one contiguous
-  // run of 4*G*K/16 bytes: a few full 16-byte-per-lane loads stage it in the
-  // wave's LDS region (instead of a 2-byte load per lane, row and segment).
-  uint8_t* wave_sc = reinterpret_cast<uint8_t*>(a_pairs + M * cstride) + wave * (4 * G) * sstride;
-  {
-    const uint32_t run = (uint32_t)(4 * G) * sstride, base = (uint32_t)n0 * sstride;
-    for (uint32_t off = 16 * lane; off < run; off += 1024) {
-      const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(ws, base + off, 0, 0);
-      *reinterpret_cast<u4_t*>(wave_sc + off) = v;
-    }
-  }
-  const int a_blocks = M * (K >> 4);
-  for (int blk = threadIdx.x; blk < a_blocks; blk += blockDim.x) {
-    const uint32_t m = (uint32_t)blk / sstride, kb = (uint32_t)blk - m * sstride;
-    const u2_t cc = __builtin_amdgcn_raw_buffer_load_b64(ac, m * cstride + kb * 8, 0, 0);
-    const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b8(as, m * sstride + kb, 0, 0);
-    const _Float16 sc = (_Float16)e4m3_to_f32(sb);
-    h8_t* dst = reinterpret_cast<h8_t*>(a_pairs + m * cstride + kb * 8);
-    dst[0] = dequant8(cc.x, sc);
-    dst[1] = dequant8(cc.y, sc);
-  }
-  __syncthreads();
-
-  float acc[G][MR];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int m = 0; m < MR; ++m) acc[g][m] = 0.f;
-
-  auto compute_unit = [&](const GUnit<G>& u, int seg) {
-    h2_t av[MR][16];
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      const h8_t* src = reinterpret_cast<const h8_t*>(a_pairs + (m < M ? m : 0) * cstride + seg * 256 + 16 * c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const h8_t v = src[i];
-        av[m][4 * i + 0] = h2_t{v[0], v[1]};
-        av[m][4 * i + 1] = h2_t{v[2], v[3]};
-        av[m][4 * i + 2] = h2_t{v[4], v[5]};
-        av[m][4 * i + 3] = h2_t{v[6], v[7]};
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint32_t sb = *reinterpret_cast<const uint16_t*>(wave_sc + (4 * g + rr) * sstride + seg * 32 + 2 * c);
-      const f2_t sw = __builtin_amdgcn_cvt_pk_f32_fp8(sb, false);
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        float part[MR];
-#pragma unroll
-        for (int m = 0; m < MR; ++m) part[m] = 0.f;
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          const uint32_t word = u.c[g][2 * b + d];
-          const h2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0);
-          const h2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1);
-          const h2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2);
-          const h2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3);
-#pragma unroll
-          for (int m = 0; m < MR; ++m) {
-            const int e = 8 * b + 4 * d;
-            part[m] = __builtin_amdgcn_fdot2(av[m][e + 0], w0, part[m], false);
-            part[m] = __builtin_amdgcn_fdot2(av[m][e + 1], w1, part[m], false);
-            part[m] = __builtin_amdgcn_fdot2(av[m][e + 2], w2, part[m], false);
-            part[m] = __builtin_amdgcn_fdot2(av[m][e + 3], w3, part[m], false);
-          }
-        }
-#pragma unroll
-        for (int m = 0; m < MR; ++m) acc[g][m] = __builtin_fmaf(part[m], b ? sw.y : sw.x, acc[g][m]);
-      }
-    }
-  };
-
-  for (int i0 = 0; i0 < segs; i0 += D) {
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      if (i0 + j < segs) compute_unit(ring[j], i0 + j);
-      __builtin_amdgcn_sched_barrier(0);
-      ring[j] = load_unit(i0 + j + D);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  // Sum the 16 lanes of each row in a fixed order; lane c == 0 stores.
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) acc[g][m] += __shfl_xor(acc[g][m], off, 16);
-  if (c != 0) return;
-  const float gg = (*p.ga) * (*p.gw);
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int n = n0 + 4 * g + rr;
-    if (n >= N) continue;
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-      if (m >= M) continue;
-      const float v = acc[g][m] * gg;
-      const int64_t o = (int64_t)m * N + n;
-      if constexpr (OUT_BF16) {
-        reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16_rne(v);
-      } else {
-        reinterpret_cast<float*>(p.out)[o] = v;
-      }
-    }
-  }
-}
-
-template <int MR, int G, int D>
-hipError_t launch_gemv(const GemmArgs& a, int waves_per_wg, hipStream_t stream) {
-  const int64_t groups = (a.N + 4 * G - 1) / (4 * G);
-  const dim3 grid((unsigned)((groups + waves_per_wg - 1) / waves_per_wg));
-  const size_t lds = (size_t)MR * a.K * 2 + (size_t)waves_per_wg * 4 * G * (a.K / 16);  // f16 activation rows + scale runs
-  if (a.out_bf16) gemv_valu_kernel<MR, G, D, true><<<grid, 64 * waves_per_wg, lds, stream>>>(a);
-  else gemv_valu_kernel<MR, G, D, false><<<grid, 64 * waves_per_wg, lds, stream>>>(a);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
 // Memory-order GEMV for M <= 2 (single-stream decode), K >= 2048, K % 256 == 0.
 // Measured on MI355X: reading the weight matrix as many rows at once in
 // 256-byte pieces leaves DRAM pages mostly unused (request latency ~3x that
@@ -807,6 +616,7 @@ __global__ __launch_bounds__(512) void gemv_flat_kernel(GemmArgs p, int R) {
   }
 }
 
+
 // Compute units of the current device (cached per device).
 int device_cus() {
   static int cus[64] = {0};
@@ -820,35 +630,32 @@ int device_cus() {
   return cus[dev];
 }
 
-// Rows per wave for the memory-order GEMV: the grid is a whole multiple
-// (`per_cu`) of the compute-unit count, so that every CU streams the same
-// number of rows (a grid of, say, 1.5 workgroups per CU leaves half the CUs
-// idle for the last third of the kernel).
-int flat_rows_per_wave(const GemmArgs& a, int waves_per_wg, int per_cu) {
-  const int64_t waves = (int64_t)device_cus() * per_cu * waves_per_wg;
-  return (int)((a.N + waves - 1) / waves);
+// Memory-order GEMV launch: 4 waves per workgroup and a grid of one
+// workgroup per CU, so that every CU streams the same number of rows (a grid
+// of, say, 1.5 workgroups per CU leaves half the CUs idle for the last third
+// of the kernel); R rows per wave.
+constexpr int kFlatWaves = 4;
+
+int flat_rows_per_wave(const GemmArgs& a) {
+  const int64_t waves = (int64_t)device_cus() * kFlatWaves;
+  const int64_t r = (a.N + waves - 1) / waves;
+  return (int)(r < 1 ? 1 : r);
 }
 
-size_t flat_lds_bytes(const GemmArgs& a, int waves_per_wg, int R, int MR) {
-  return (size_t)MR * a.K * 2 + (size_t)waves_per_wg * (R * MR * 64 * 4 + 1024);
+size_t flat_lds_bytes(const GemmArgs& a, int R) {
+  return (size_t)a.M * a.K * 2 + (size_t)kFlatWaves * (R * a.M * 64 * 4 + 1024);
 }
 
 template <int MR>
-hipError_t launch_gemv_flat(const GemmArgs& a, int waves_per_wg, int R, hipStream_t stream) {
+hipError_t launch_flat_mr(const GemmArgs& a, int R, hipStream_t stream) {
   const int64_t waves = (a.N + R - 1) / R;
-  const dim3 grid((unsigned)((waves + waves_per_wg - 1) / waves_per_wg));
-  const size_t lds = flat_lds_bytes(a, waves_per_wg, R, MR);
-  const bool nt = env_int("NVFP4_FLAT_NT", 1) != 0;  // non-temporal weight stream
-  if (a.out_bf16) {
-    if (nt) gemv_flat_kernel<MR, 2, true><<<grid, 64 * waves_per_wg, lds, stream>>>(a, R);
-    else gemv_flat_kernel<MR, 0, true><<<grid, 64 * waves_per_wg, lds, stream>>>(a, R);
-  } else {
-    if (nt) gemv_flat_kernel<MR, 2, false><<<grid, 64 * waves_per_wg, lds, stream>>>(a, R);
-    else gemv_flat_kernel<MR, 0, false><<<grid, 64 * waves_per_wg, lds, stream>>>(a, R);
-  }
+  const dim3 grid((unsigned)((waves + kFlatWaves - 1) / kFlatWaves));
+  const size_t lds = flat_lds_bytes(a, R);
+  // the weight stream is read once: non-temporal loads
+  if (a.out_bf16) gemv_flat_kernel<MR, 2, true><<<grid, 64 * kFlatWaves, lds, stream>>>(a, R);
+  else gemv_flat_kernel<MR, 2, false><<<grid, 64 * kFlatWaves, lds, stream>>>(a, R);
   return hipGetLastError();
 }
-
 
 template <int NT, int VB, int D>
 hipError_t launch_cfg(const GemmArgs& a, int kw, hipStream_t stream) {
@@ -861,17 +668,6 @@ hipError_t launch_cfg(const GemmArgs& a, int kw, hipStream_t stream) {
   }
   return hipGetLastError();
 }
-
-template <int VB>
-hipError_t launch_vb(const GemmArgs& a, int nt, int kw, hipStream_t stream) {
-  switch (nt) {
-    case 1: return launch_cfg<1, VB, 8>(a, kw, stream);
-    case 2: return launch_cfg<2, VB, 8>(a, kw, stream);
-    default: return launch_cfg<4, VB, 4>(a, kw, stream);
-  }
-}
-
-}  // namespace
 
 // Dynamic LDS of the ALDS mode: every wave's f16 activation rows plus the
 // 64-byte zero run (must match the layout in the kernel).
@@ -894,92 +690,76 @@ hipError_t launch256(const GemmArgs& a, int kw, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int NT, int D>
-hipError_t launch256(const GemmArgs& a, int kw, bool alds, hipStream_t stream) {
-  return alds ? launch256<NT, D, true>(a, kw, stream) : launch256<NT, D, false>(a, kw, stream);
+}  // namespace
+
+// One or two rows, K a multiple of 256 from 2048 on, the f16 activation rows,
+// the per-row slots and the fill within the kernel's limits.
+bool gemv_flat_supported(const GemmArgs& a) {
+  if (a.M < 1 || a.M > 2 || a.K < 2048 || a.K % 256 != 0) return false;
+  const int R = flat_rows_per_wave(a);
+  return R * a.M <= 64 && flat_lds_bytes(a, R) <= 64 * 1024 &&
+         (int64_t)a.M * (a.K / 16) <= (int64_t)64 * kFlatWaves * kFlatAB;
 }
 
-// Launch choice.  K % 256 == 0 takes the fast path.  Measured on MI355X
-// (sweep over NT x D x KW): a few hundred to a few thousand resident waves with
-// 2-3 units in flight each do best; deeper rings or more, shorter waves only
-// add pressure on the vector L1.  NT = 2 amortizes the activation operand when
-// M > 1; KW is the smallest power of two that gives >= 600 waves while every
-// wave keeps >= 4 units.  NVFP4_SKINNY_NT, NVFP4_SKINNY_KW and NVFP4_SKINNY_D
-// override the choice (tuning knobs; results change only by fp32 summation
-// order).  Other K take the general path.
-hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
-  const int64_t tiles16 = (a.N + 15) / 16;
-  const int64_t mtiles = (a.M + 15) / 16;
-  const int e_nt = env_int("NVFP4_SKINNY_NT", 0);
-  const int e_kw = env_int("NVFP4_SKINNY_KW", 0);
-  const int e_d = env_int("NVFP4_SKINNY_D", 0);
-  const bool kw_ok = e_kw == 1 || e_kw == 2 || e_kw == 4 || e_kw == 8;
-  // VALU GEMV for one or two activation rows (K a multiple of 512 and the
-  // f16 activation rows within 64 KiB of LDS).  NVFP4_GEMV=0 disables it;
-  // NVFP4_GEMV_G (rows per wave / 4) and NVFP4_GEMV_W (waves per workgroup)
-  // are tuning knobs.
-  const int e_gemv = env_int("NVFP4_GEMV", 3);
-  if (e_gemv == 3 && gemv_fp4_supported(a)) return launch_gemv_fp4(a, stream);
-  if (a.M >= 3 && a.M <= 16 && env_int("NVFP4_M16", 1) != 0 && gemm_m16_preferred(a)) return launch_gemm_m16(a, stream);
-  if (e_gemv >= 2 && a.M <= 2 && a.K >= 2048 && a.K % 256 == 0) {
-    int e_w = env_int("NVFP4_GEMV_W", 4);
-    if (e_w != 4 && e_w != 8) e_w = 4;
-    int R = flat_rows_per_wave(a, e_w, env_int("NVFP4_FLAT_C", 1));
-    if (R < 1) R = 1;
-    if (R * a.M <= 64 && flat_lds_bytes(a, e_w, R, a.M) <= 64 * 1024 &&
-        (int64_t)a.M * (a.K / 16) <= (int64_t)64 * e_w * kFlatAB) {
-      return a.M == 1 ? launch_gemv_flat<1>(a, e_w, R, stream) : launch_gemv_flat<2>(a, e_w, R, stream);
-    }
-  }
-  if (e_gemv != 0 && a.M <= 2 && a.K % 512 == 0 && (int64_t)a.M * a.K * 2 + 4 * 16 * (a.K / 16) <= 64 * 1024) {
-    const int e_g = env_int("NVFP4_GEMV_G", 2);
-    int e_w = env_int("NVFP4_GEMV_W", 4);
-    if (e_w != 1 && e_w != 2 && e_w != 4) e_w = 4;
-    if (a.M == 1) {
-      if (e_g == 1) return launch_gemv<1, 1, 4>(a, e_w, stream);
-      if (e_g == 4) return launch_gemv<1, 4, 3>(a, e_w, stream);
-      return launch_gemv<1, 2, 4>(a, e_w, stream);
-    }
-    return launch_gemv<2, 2, 4>(a, e_w, stream);
-  }
-  if (a.K % 256 == 0) {
-    int nt = a.M > 1 ? 2 : 1;
-    if (e_nt == 1 || e_nt == 2) nt = e_nt;
-    const int64_t wgs = ((tiles16 + nt - 1) / nt) * mtiles;
-    const int64_t units = a.K / 256;
-    // activations in LDS when they are few: a handful of rows whose f16 copy
-    // stays small (measured faster for M = 1; M = 16 streams them instead)
-    const bool small_m = a.M <= 4;
-    int kw = 1;
-    while (kw < kMaxWavesK && (small_m ? wgs * kw < 4096 : wgs * kw < 600) && units / (2 * kw) >= 4) kw *= 2;
-    if (kw_ok) kw = e_kw;
-    const int e_alds = env_int("NVFP4_SKINNY_ALDS", -1);
-    bool alds = small_m && alds_bytes(a, kw) <= 48 * 1024;
-    if (e_alds == 0 || e_alds == 1) alds = e_alds == 1 && alds_bytes(a, kw) <= 48 * 1024;
-    const int d = (e_d == 2 || e_d == 3 || e_d == 4 || e_d == 6) ? e_d : (nt == 1 ? 3 : 2);
-    if (nt == 2) {
-      switch (d) {
-        case 3: return launch256<2, 3>(a, kw, alds, stream);
-        case 4: case 6: return launch256<2, 4>(a, kw, alds, stream);
-        default: return launch256<2, 2>(a, kw, alds, stream);
-      }
-    }
-    switch (d) {
-      case 2: return launch256<1, 2>(a, kw, alds, stream);
-      case 4: return launch256<1, 4>(a, kw, alds, stream);
-      case 6: return launch256<1, 6>(a, kw, alds, stream);
-      default: return launch256<1, 3>(a, kw, alds, stream);
-    }
-  }
+hipError_t launch_gemv_flat(const GemmArgs& a, hipStream_t stream) {
+  const int R = flat_rows_per_wave(a);
+  return a.M == 1 ? launch_flat_mr<1>(a, R, stream) : launch_flat_mr<2>(a, R, stream);
+}
+
+// K % 256 == 0, any M (16 rows per grid.y).  Measured on MI355X (sweep over
+// tiles per workgroup NT, ring depth D and waves per workgroup KW): a few
+// hundred to a few thousand resident waves with 2-3 units in flight each do
+// best; deeper rings or more, shorter waves only add pressure on the vector
+// L1.  NT = 2 amortizes the activation operand when M > 1; KW is the smallest
+// power of two that gives enough waves (>= 4096 with activations in LDS,
+// which is faster for M <= 4; >= 600 otherwise) while every wave keeps >= 4
+// units.
+hipError_t launch_gemm_skinny256(const GemmArgs& a, hipStream_t stream) {
+  const int nt = a.M > 1 ? 2 : 1;
+  const int64_t wgs = ((a.N + 16 * nt - 1) / (16 * nt)) * ((a.M + 15) / 16);
+  const int64_t units = a.K / 256;
+  const bool small_m = a.M <= 4;
+  int kw = 1;
+  while (kw < kMaxWavesK && (small_m ? wgs * kw < 4096 : wgs * kw < 600) && units / (2 * kw) >= 4) kw *= 2;
+  const bool alds = small_m && alds_bytes(a, kw) <= 48 * 1024;
+  if (nt == 2) return alds ? launch256<2, 2, true>(a, kw, stream) : launch256<2, 2, false>(a, kw, stream);
+  return alds ? launch256<1, 3, true>(a, kw, stream) : launch256<1, 3, false>(a, kw, stream);
+}
+
+// Any K (a multiple of 16), any M: 64 VB-element super-steps (VB = 2 when the
+// rows are 16-byte aligned), two 16-row tiles per workgroup once there are
+// 1024 tiles, KW as above for >= 1536 waves.
+hipError_t launch_gemm_skinny16(const GemmArgs& a, hipStream_t stream) {
+  const int64_t tiles16 = (a.N + 15) / 16, mtiles = (a.M + 15) / 16;
   const int vb = (a.K % 32 == 0) ? 2 : 1;
-  int nt = (tiles16 * mtiles >= 1024) ? 2 : 1;
-  if (e_nt == 1 || e_nt == 2 || e_nt == 4) nt = e_nt;
+  const int nt = (tiles16 * mtiles >= 1024) ? 2 : 1;
   const int64_t wgs = ((tiles16 + nt - 1) / nt) * mtiles;
   const int64_t steps = (a.K + 64 * vb - 1) / (64 * vb);
   int kw = 1;
   while (kw < kMaxWavesK && wgs * kw < 1536 && steps / (2 * kw) >= 4) kw *= 2;
-  if (kw_ok) kw = e_kw;
-  return vb == 2 ? launch_vb<2>(a, nt, kw, stream) : launch_vb<1>(a, nt, kw, stream);
+  if (vb == 2) return nt == 2 ? launch_cfg<2, 2, 8>(a, kw, stream) : launch_cfg<1, 2, 8>(a, kw, stream);
+  return nt == 2 ? launch_cfg<2, 1, 8>(a, kw, stream) : launch_cfg<1, 1, 8>(a, kw, stream);
+}
+
+// The weight-streaming path's kernel for a product: the FP4 GEMV (one or two
+// rows, K a multiple of 1024 up to 8192), the M-tile kernel (3..16 rows where
+// it is faster: long K, or many rows), the memory-order GEMV (one or two rows,
+// other K from 2048 on), else the skinny kernels.
+int skinny_kernel_choice(const GemmArgs& a) {
+  if (gemv_fp4_supported(a)) return kKernelGemvFp4;
+  if (gemm_m16_preferred(a)) return kKernelM16;
+  if (gemv_flat_supported(a)) return kKernelGemvFlat;
+  return a.K % 256 == 0 ? kKernelSkinny256 : kKernelSkinny16;
+}
+
+hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
+  switch (skinny_kernel_choice(a)) {
+    case kKernelGemvFp4: return launch_gemv_fp4(a, stream);
+    case kKernelM16: return launch_gemm_m16(a, stream);
+    case kKernelGemvFlat: return launch_gemv_flat(a, stream);
+    case kKernelSkinny256: return launch_gemm_skinny256(a, stream);
+    default: return launch_gemm_skinny16(a, stream);
+  }
 }
 
 }  // namespace nvfp4

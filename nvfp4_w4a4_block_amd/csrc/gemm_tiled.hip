@@ -657,14 +657,17 @@ hipError_t launch_persistent(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+bool gemm_tiled_persistent_supported(const GemmArgs& a) { return persistent_ok(a); }
+
 bool gemm_tiled_quant_out_supported(const GemmArgs& a) { return persistent_ok(a) && a.N % 16 == 0; }
 
-hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
-  if (persistent_ok(a)) {
-    const bool q = a.y_codes != nullptr && a.N % 16 == 0;
-    if (a.out_bf16) return q ? launch_persistent<true, true>(a, stream) : launch_persistent<true, false>(a, stream);
-    return q ? launch_persistent<false, true>(a, stream) : launch_persistent<false, false>(a, stream);
-  }
+hipError_t launch_gemm_tiled_persistent(const GemmArgs& a, hipStream_t stream) {
+  const bool q = a.y_codes != nullptr && a.N % 16 == 0;
+  if (a.out_bf16) return q ? launch_persistent<true, true>(a, stream) : launch_persistent<true, false>(a, stream);
+  return q ? launch_persistent<false, true>(a, stream) : launch_persistent<false, false>(a, stream);
+}
+
+hipError_t launch_gemm_tiled_simple(const GemmArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM));
   const bool k32 = a.K % 32 == 0;
   if (k32) {
@@ -675,6 +678,10 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
     else gemm_tiled_kernel<false, false><<<grid, kThreads, 0, stream>>>(a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
+  return persistent_ok(a) ? launch_gemm_tiled_persistent(a, stream) : launch_gemm_tiled_simple(a, stream);
 }
 
 }  // namespace nvfp4

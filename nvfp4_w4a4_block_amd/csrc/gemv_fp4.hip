@@ -348,11 +348,6 @@ __global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
   }
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
-}
-
 int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
@@ -408,8 +403,6 @@ bool gemv_fp4_supported(const GemmArgs& a) {
 hipError_t launch_gemv_fp4(const GemmArgs& a, hipStream_t stream) {
   const int64_t target_waves = (int64_t)device_cus() * 6;
   int G = (int)((a.N + 8 * target_waves / 2) / (8 * target_waves));
-  const int e_g = env_int("NVFP4_FP4_G", 0);
-  if (e_g > 0) G = e_g;
   if (G < 1) G = 1;
   while (G > 1 && ((int64_t)G * a.K / 2 > kScaleLoads * 1024 || fp4_lds_bytes(a.M, a.K, G) > 64 * 1024)) --G;
   return a.M == 1 ? launch_fp4_k<1>(a, G, stream) : launch_fp4_k<2>(a, G, stream);

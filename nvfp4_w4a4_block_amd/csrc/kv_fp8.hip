@@ -150,57 +150,34 @@ __global__ __launch_bounds__(256) void kv_decode_kernel(const uint8_t* q, int64_
   }
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
-}
+// Grid-stride launch: at most 16384 workgroups, two 16-element chunks per
+// thread and pass with all their loads in flight.  A sweep on MI355X over one
+// layer's K and V (48.2M elements) found 2 chunks x 16384 workgroups about 5%
+// faster than 4 x 4096 and the other points within noise.
+constexpr int kKvChunks = 2;
+constexpr int64_t kKvMaxGrid = 16384;
 
-// Grid-stride launch: at most NVFP4_KV_GRID workgroups (default 16384),
-// NVFP4_KV_CHUNKS (2, 4 or 8; default 2) 16-element chunks per thread and pass
-// with all their loads in flight (tuning knobs; results do not change).  A
-// sweep on MI355X over one layer's K and V (48.2M elements) found 2 x 16384
-// about 5% faster than 4 x 4096 and the rest within noise.
 unsigned grid_for(int64_t n) {
   const int64_t chunks = n / 16;
   int64_t g = (chunks + 255) / 256;
-  int64_t cap = env_int("NVFP4_KV_GRID", 16384);
-  if (cap < 1) cap = 16384;
-  if (g > cap) g = cap;
+  if (g > kKvMaxGrid) g = kKvMaxGrid;
   return (unsigned)(g < 1 ? 1 : g);
-}
-
-template <int C>
-hipError_t encode_c(const void* x, bool bf16, int64_t n, const float* scale, uint8_t* q, hipStream_t stream) {
-  if (bf16) kv_encode_kernel<true, C><<<grid_for(n), 256, 0, stream>>>(x, n, scale, q);
-  else kv_encode_kernel<false, C><<<grid_for(n), 256, 0, stream>>>(x, n, scale, q);
-  return hipGetLastError();
-}
-
-template <int C>
-hipError_t decode_c(const uint8_t* q, int64_t n, const float* scale, void* x, bool bf16, hipStream_t stream) {
-  if (bf16) kv_decode_kernel<true, C><<<grid_for(n), 256, 0, stream>>>(q, n, scale, x);
-  else kv_decode_kernel<false, C><<<grid_for(n), 256, 0, stream>>>(q, n, scale, x);
-  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_kv_fp8_encode(const void* x, bool bf16, int64_t n, const float* scale, uint8_t* q,
                                 hipStream_t stream) {
-  switch (env_int("NVFP4_KV_CHUNKS", 2)) {
-    case 4: return encode_c<4>(x, bf16, n, scale, q, stream);
-    case 8: return encode_c<8>(x, bf16, n, scale, q, stream);
-    default: return encode_c<2>(x, bf16, n, scale, q, stream);
-  }
+  if (bf16) kv_encode_kernel<true, kKvChunks><<<grid_for(n), 256, 0, stream>>>(x, n, scale, q);
+  else kv_encode_kernel<false, kKvChunks><<<grid_for(n), 256, 0, stream>>>(x, n, scale, q);
+  return hipGetLastError();
 }
 
 hipError_t launch_kv_fp8_decode(const uint8_t* q, int64_t n, const float* scale, void* x, bool bf16,
                                 hipStream_t stream) {
-  switch (env_int("NVFP4_KV_CHUNKS", 2)) {
-    case 4: return decode_c<4>(q, n, scale, x, bf16, stream);
-    case 8: return decode_c<8>(q, n, scale, x, bf16, stream);
-    default: return decode_c<2>(q, n, scale, x, bf16, stream);
-  }
+  if (bf16) kv_decode_kernel<true, kKvChunks><<<grid_for(n), 256, 0, stream>>>(q, n, scale, x);
+  else kv_decode_kernel<false, kKvChunks><<<grid_for(n), 256, 0, stream>>>(q, n, scale, x);
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4

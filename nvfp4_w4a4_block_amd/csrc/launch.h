@@ -74,27 +74,61 @@ hipError_t launch_argmax_rows(const float* logits, int M, int N, uint64_t* keys,
 hipError_t launch_tree_accept(int n, const int32_t* parent, const int32_t* draft, const int32_t* greedy_in,
                               uint64_t* keys, int32_t* greedy_out, int32_t* result, hipStream_t stream);
 
-// Weight-streaming path (built for M <= 16; tiles larger M by 16 rows).
+// Kernels of the product, numbered as the kernel selectors of nvfp4_path in
+// include/nvfp4.h.
+enum KernelId : int {
+  kKernelGemvFp4 = 3,          // gemv_fp4_kernel: FP4 matrix-core GEMV, M <= 2
+  kKernelGemvFlat = 4,         // gemv_flat_kernel: memory-order GEMV, M <= 2
+  kKernelM16 = 5,              // gemm_m16_kernel: weight streaming on f16 matrix cores, M <= 16
+  kKernelSkinny256 = 6,        // gemm_skinny256_kernel: K % 256 == 0, any M
+  kKernelSkinny16 = 7,         // gemm_skinny_kernel: any K, any M
+  kKernelTiledPersistent = 8,  // gemm_wg_tiled_kernel: K % 1024 == 0
+  kKernelTiled = 9,            // gemm_tiled_kernel: any shape
+};
+
+// Weight-streaming path (built for M <= 16; the skinny kernels tile larger M
+// by 16 rows): skinny_kernel_choice() names the kernel launch_gemm_skinny()
+// runs.
+int skinny_kernel_choice(const GemmArgs& a);
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
 
-// FP4 matrix-core GEMV for M <= 2 (K % 256 == 0, K <= 16384 within its LDS
-// budget); launch only where gemv_fp4_supported() holds.
+// FP4 matrix-core GEMV for M <= 2 (K % 1024 == 0, 1024 <= K <= 8192 within
+// its LDS budget); launch only where gemv_fp4_supported() holds.
 bool gemv_fp4_supported(const GemmArgs& a);
 hipError_t launch_gemv_fp4(const GemmArgs& a, hipStream_t stream);
 
-// Weight-streaming GEMM for M <= 16 on f16 matrix cores (K % 128 == 0; without
-// a workspace K <= 7168).  gemm_m16_workspace_bytes() is the workspace that
-// lets it split K over workgroups (0 when it would not).
+// Memory-order GEMV for M <= 2 (K % 256 == 0, K >= 2048, within its limits).
+bool gemv_flat_supported(const GemmArgs& a);
+hipError_t launch_gemv_flat(const GemmArgs& a, hipStream_t stream);
+
+// Skinny kernels: K % 256 == 0, and any K (a multiple of 16); any M.
+hipError_t launch_gemm_skinny256(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_skinny16(const GemmArgs& a, hipStream_t stream);
+
+// Weight-streaming GEMM for 1 <= M <= 16 on f16 matrix cores (K % 128 == 0;
+// any K in one pass).  gemm_m16_workspace_bytes() is the workspace that lets
+// it split K over workgroups (0 when it would not).
 bool gemm_m16_supported(const GemmArgs& a);
 bool gemm_m16_small_prefers_skinny(const GemmArgs& a);  // the skinny kernel serves this product instead
-bool gemm_m16_preferred(const GemmArgs& a);  // supported, and not starved of workgroups unsplit
+bool gemm_m16_preferred(const GemmArgs& a);  // 3 <= M <= 16, supported, and faster than the alternatives
 int64_t gemm_m16_workspace_bytes(const GemmArgs& a);
 hipError_t launch_gemm_m16(const GemmArgs& a, hipStream_t stream);
 
-// LDS-tiled MFMA path for large M.  gemm_tiled_quant_out_supported() tells
-// whether launch_gemm_tiled() honours y_codes (the persistent kernel: K %
-// 1024 == 0, N % 16 == 0); launch_gemm_tiled() ignores y_codes otherwise.
+// LDS-tiled MFMA path for large M: the persistent kernel where
+// gemm_tiled_persistent_supported() holds (K % 1024 == 0), else the simple
+// tiled kernel.  gemm_tiled_quant_out_supported() tells whether
+// launch_gemm_tiled() honours y_codes (the persistent kernel with N % 16 ==
+// 0); launch_gemm_tiled() ignores y_codes otherwise.
+bool gemm_tiled_persistent_supported(const GemmArgs& a);
+hipError_t launch_gemm_tiled_persistent(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_tiled_simple(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
 bool gemm_tiled_quant_out_supported(const GemmArgs& a);
+
+// Read-only stream over two arrays (stream.hip): the measured read ceiling
+// of a weight matrix's codes and scales.  sink[0] is written only if the XOR
+// of everything read equals `magic`.
+hipError_t launch_read_stream(const uint8_t* a, int64_t a_bytes, const uint8_t* b, int64_t b_bytes, uint32_t* sink,
+                              uint32_t magic, hipStream_t stream);
 
 }  // namespace nvfp4

@@ -42,7 +42,7 @@ def test_status_strings_and_version(lib):
     for s in range(6):
         assert B.status_string(s)
     assert B.status_string(99) == "unknown status"
-    assert lib.nvfp4_abi_version() == 8
+    assert lib.nvfp4_abi_version() == 9
 
 
 def gemm(lib, M, K, N, ptrs=(A16,) * 7, out_dt=B.NVFP4_BF16, path=B.PATH_AUTO):
@@ -71,7 +71,38 @@ def test_gemm_rejects_null_align_dtype_path(lib):
     # scalar scale pointers only need 4-byte alignment: this one passes validation up to the
     # dtype check, which fails first here
     assert gemm(lib, 1, 32, 16, ptrs=(A16,) * 2 + (A16 + 4,) + (A16,) * 4, out_dt=7) == B.NVFP4_ERR_DTYPE
-    assert gemm(lib, 1, 32, 16, path=3) == B.NVFP4_ERR_DTYPE
+    assert gemm(lib, 1, 32, 16, path=10) == B.NVFP4_ERR_DTYPE
+    assert gemm(lib, 1, 32, 16, path=-1) == B.NVFP4_ERR_DTYPE
+
+
+def test_gemm_kernel_selectors_refuse_shapes_they_do_not_take(lib):
+    """An explicitly selected kernel that does not take the product is refused (the checks below
+    decide on the shape alone, before any HIP call)."""
+    assert gemm(lib, 1, 32, 16, path=B.KERNEL_GEMV_FP4) == B.NVFP4_ERR_SHAPE      # K % 1024 != 0
+    assert gemm(lib, 3, 1024, 16, path=B.KERNEL_GEMV_FP4) == B.NVFP4_ERR_SHAPE    # M > 2
+    assert gemm(lib, 1, 32, 16, path=B.KERNEL_GEMV_FLAT) == B.NVFP4_ERR_SHAPE     # K < 2048
+    assert gemm(lib, 17, 128, 16, path=B.KERNEL_M16) == B.NVFP4_ERR_SHAPE         # M > 16
+    assert gemm(lib, 4, 144, 16, path=B.KERNEL_M16) == B.NVFP4_ERR_SHAPE          # K % 128 != 0
+    assert gemm(lib, 4, 144, 16, path=B.KERNEL_SKINNY256) == B.NVFP4_ERR_SHAPE    # K % 256 != 0
+    assert gemm(lib, 40, 1280, 16, path=B.KERNEL_TILED_PERSISTENT) == B.NVFP4_ERR_SHAPE  # K % 1024 != 0
+    assert gemm(lib, 0, 32, 16, ptrs=(0,) * 7, path=B.KERNEL_GEMV_FP4) == B.NVFP4_OK  # empty: nothing to run
+    assert gemm(lib, 1 << 21, 16, 16, path=B.KERNEL_SKINNY16) == B.NVFP4_ERR_SHAPE   # grid rows > 65535
+
+
+def test_gemm_dispatch_host_cases(lib):
+    """nvfp4_gemm_dispatch on shapes decided without a device query: invalid or empty products
+    (0), one or two rows with K a multiple of 1024 up to 8192 (the FP4 GEMV), more than 16 rows
+    (the persistent tiled kernel for K % 1024 == 0, else the simple one)."""
+    f = lib.nvfp4_gemm_dispatch
+    assert f(0, 5120, 100, 0) == 0
+    assert f(1, 5120, 0, 0) == 0
+    assert f(1, 24, 100, 0) == 0
+    assert f(1, 5120, 100, -1) == 0
+    assert f(1, 5120, 25600, 0) == B.KERNEL_GEMV_FP4
+    assert f(2, 1024, 7, 0) == B.KERNEL_GEMV_FP4
+    assert f(512, 5120, 25600, 0) == B.KERNEL_TILED_PERSISTENT
+    assert f(512, 25600, 5120, 0) == B.KERNEL_TILED_PERSISTENT
+    assert f(17, 768, 100, 0) == B.KERNEL_TILED
     assert lib.nvfp4_gemm(1, 32, 16, A16, A16, A16, A16, A16, A16, A16, 2, None) == B.NVFP4_ERR_DTYPE
 
 
@@ -110,9 +141,10 @@ def test_gemm_quantize_output_validation(lib):
 
 
 def test_gemm_workspace_bytes_host_cases(lib):
-    """Shapes the split path never takes need no workspace (decided on the host, no HIP call):
-    one or two rows (the GEMV), more than 16 rows (the tiled path), K not a multiple of 128,
-    short-K products with N <= 16384 (the skinny kernel), invalid shapes."""
+    """Shapes the split path never takes need no workspace (decided from the shape alone, before
+    any device query): one or two rows (the GEMV), more than 16 rows (the tiled path), K not a
+    multiple of 128, short-K products with N <= 16384 (the skinny kernel), invalid shapes.  The
+    shapes that do split depend on the device's compute-unit count and are checked on the GPU."""
     f = lib.nvfp4_gemm_workspace_bytes
     assert f(1, 25600, 5120) == 0
     assert f(2, 25600, 5120) == 0
@@ -124,7 +156,6 @@ def test_gemm_workspace_bytes_host_cases(lib):
     assert f(-1, 256, 64) == 0
     assert f(16, 5120, 5120) == 0  # short K, N <= 16384: the skinny kernel, unsplit
     assert f(16, 8192, 16384) == 0
-    assert f(16, 25600, 5120) > 0  # the tree-verification down-projection splits K
 
 
 def test_empty_gemm_is_ok_without_pointers(lib):
@@ -218,7 +249,7 @@ def test_tree_entry_points_validate(lib):
     assert verify(16, 5120, 100, tuple(ptrs)) == B.NVFP4_ERR_ALIGN
     ptrs[10] = None
     assert verify(16, 5120, 100, tuple(ptrs)) == B.NVFP4_ERR_NULL
-    # logits may be omitted only where the argmax is fused (K % 256 == 0, K <= 5120)
+    # logits may be omitted only where the argmax is fused (K % 128 == 0)
     assert verify(16, 1040, 100, logits=None) == B.NVFP4_ERR_NULL
 
 

@@ -9,8 +9,6 @@ long rows of NVFP4 weights.  Bar: |gpu - C| <= 1e-3 * sum_k |a_hat * w_hat| per 
 the bf16 rounding of the stored value), C the oracle's fp64 product; the split path must be
 bit-identical from run to run and leave its counters at zero.
 """
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -22,27 +20,10 @@ from oracle import quant as Q
 
 pytestmark = pytest.mark.gpu
 
-KNOBS = ("NVFP4_M16_G", "NVFP4_M16_RB", "NVFP4_M16_KS", "NVFP4_M16_KZ", "NVFP4_M16_D", "NVFP4_M16_CP",
-         "NVFP4_M16_AW", "NVFP4_M16_SB", "NVFP4_M16_SMALL")
-
 
 @pytest.fixture(scope="module", autouse=True)
 def _lib():
     U.require_gpu_lib()
-
-
-@pytest.fixture()
-def knobs():
-    """Sets launch-plan knobs for one test and clears them afterwards."""
-    set_ = {}
-
-    def apply(**kv):
-        for k, v in kv.items():
-            os.environ[f"NVFP4_M16_{k}"] = str(v)
-            set_[k] = v
-    yield apply
-    for k in KNOBS:
-        os.environ.pop(k, None)
 
 
 def _pair(M, K, N, seed):
@@ -60,48 +41,45 @@ def _pair(M, K, N, seed):
     return (ac, asc, U.scalar(g_a), wc, ws, gw), C, T
 
 
-# (M, K, N): one line (K = 128), odd line counts, the largest K staged whole (49 lines), K
-# beyond that (split required, else the older kernels), N of 1, ragged and several row blocks.
+# (M, K, N): one line (K = 128), odd line counts, 49 and 50 lines, K beyond the whole-range scale
+# staging (64 lines: the 8-line scale blocks), N of 1, ragged and several row blocks.
 CASES = [(3, 128, 1), (5, 384, 37), (16, 1024, 300), (7, 2688, 129), (16, 6272, 64), (16, 6400, 100),
-         (16, 9216, 1000), (11, 25600, 300), (16, 5120, 3000), (4, 640, 2049)]
+         (16, 9216, 1000), (11, 25600, 300), (16, 5120, 3000), (4, 640, 2049), (1, 3456, 333), (2, 8320, 129)]
 
 
-@pytest.mark.parametrize("small", [1, 0], ids=["dispatch", "m16-forced"])
 @pytest.mark.parametrize("M,K,N", CASES)
-def test_m16_with_and_without_workspace(M, K, N, small, knobs):
-    """small=1: the library's dispatch (short-K products with N <= 16384 run the skinny kernel);
-    small=0: the M-tile kernel for every shape it supports."""
-    knobs(SMALL=small)
+def test_m16_with_and_without_workspace(M, K, N):
+    """The library's dispatch without and with a workspace (short-K products with N <= 16384 run
+    the skinny kernel, long ones the M-tile kernel, split over workgroups when the workspace is
+    there), and the M-tile kernel itself for every shape, unsplit."""
     dev, C, T = _pair(M, K, N, 11 * M + K + N)
     for i, ws in enumerate((None, "auto")):
         out_dtype = torch.float32 if i == 0 else torch.bfloat16
         out = B.nvfp4_gemm(*dev, out_dtype=out_dtype, workspace=ws)
         U.assert_within(U.host(out), C, T + U.out_rounding_slack(C, out_dtype), f"M={M} K={K} N={N} ws={ws}")
+    out = B.nvfp4_gemm(*dev, out_dtype=torch.float32, path=B.KERNEL_M16)
+    U.assert_within(U.host(out), C, T, f"M={M} K={K} N={N} M-tile kernel")
 
 
-# Launch plans forced through the tuning knobs: row groups per wave (G), row blocks (RB) and K
-# slices (KS) per workgroup, K splits over workgroups (KZ), loads in flight (D), cache policy
-# (CP), activations dequantized once per workgroup into a shared f16 window (AW), weight scales
-# of the whole K range staged once per wave (SB).
-PLANS = [dict(G=1, RB=1, KS=1, KZ=1, D=1), dict(G=4, RB=2, KS=4, KZ=1, D=2), dict(G=2, RB=1, KS=8, KZ=3, D=2),
-         dict(G=1, RB=8, KS=1, KZ=7, D=4, CP=0), dict(G=4, RB=1, KS=2, KZ=13, D=1), dict(G=2, RB=4, KS=2, KZ=40, D=2, CP=2),
-         dict(G=1, RB=8, KS=1, KZ=1, D=4), dict(G=1, RB=16, KS=1, KZ=5, D=2), dict(G=1, RB=8, KS=2, KZ=2, D=1),
-         dict(G=1, RB=8, KS=1, KZ=1, D=2, AW=1), dict(G=1, RB=8, KS=1, KZ=3, D=1, AW=1),
-         dict(G=1, RB=8, KS=1, KZ=7, D=4, AW=1), dict(G=1, RB=8, KS=1, KZ=1, D=2, AW=1, SB=1),
-         dict(G=1, RB=8, KS=1, KZ=3, D=1, AW=1, SB=1), dict(G=1, RB=8, KS=1, KZ=5, D=4, AW=1, SB=1)]
+# Split shapes: the workspace plan splits K until there are about 7.5 waves per CU (at least 6
+# lines per split): few rows and a long K give many splits, a larger N fewer.
+SPLIT_CASES = [(16, 25600, 512), (16, 25600, 5120), (9, 12288, 333), (16, 10240, 2000), (3, 9216, 129)]
 
 
-@pytest.mark.parametrize("plan", PLANS, ids=lambda p: "-".join(f"{k}{v}" for k, v in p.items()))
-@pytest.mark.parametrize("M,K,N", [(16, 5120, 700), (9, 3456, 333)])
-def test_m16_forced_plans(M, K, N, plan, knobs):
-    knobs(SMALL=0, **plan)
+@pytest.mark.parametrize("M,K,N", SPLIT_CASES)
+def test_m16_split_matches_oracle(M, K, N):
+    need = int(B.load().nvfp4_gemm_workspace_bytes(M, K, N))
+    assert need > 0, "the product should split"
+    assert B.gemm_dispatch(M, K, N, need) == B.KERNEL_M16
     dev, C, T = _pair(M, K, N, 3 * M + K + N)
-    out = B.nvfp4_gemm(*dev, out_dtype=torch.float32, workspace="auto")
-    U.assert_within(U.host(out), C, T, f"M={M} K={K} N={N} plan={plan}")
+    ws = torch.zeros((need,), dtype=torch.uint8, device=U.DEV)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        out = B.nvfp4_gemm(*dev, out_dtype=out_dtype, workspace=ws)
+        U.assert_within(U.host(out), C, T + U.out_rounding_slack(C, out_dtype), f"M={M} K={K} N={N} split")
+    assert not ws[:256].any().item(), "arrival counters not reset"
 
 
-def test_m16_split_deterministic_and_counters_reset(knobs):
-    knobs(KZ=25)
+def test_m16_split_deterministic_and_counters_reset():
     M, K, N = 16, 25600, 512
     dev, C, T = _pair(M, K, N, 5)
     need = int(B.load().nvfp4_gemm_workspace_bytes(M, K, N))
@@ -118,11 +96,10 @@ def test_m16_split_deterministic_and_counters_reset(knobs):
     assert not small.any().item()
 
 
-def test_m16_split_reads_fresh_partials(knobs):
+def test_m16_split_reads_fresh_partials():
     """Two different products through one workspace, alternately: every result must match its
     own oracle, so the last workgroup of a row block never adds partial sums left over from the
     other product (or from an earlier call) instead of the ones just written."""
-    knobs(KZ=10)
     M, K, N = 16, 25600, 777
     dev1, C1, T1 = _pair(M, K, N, 21)
     dev2, C2, T2 = _pair(M, K, N, 22)
@@ -135,6 +112,23 @@ def test_m16_split_reads_fresh_partials(knobs):
         U.assert_within(o2.cpu().numpy(), C2, T2, "product 2")
 
 
+def _replays_match(call, out, eager):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), eager.view(torch.int32))
+
+
 def test_m16_split_graph_replays():
     """The split kernel inside a replayed HIP graph: every replay equals the eager result (the
     counters return to zero, so nothing needs clearing between replays)."""
@@ -144,19 +138,20 @@ def test_m16_split_graph_replays():
     assert ws is not None
     eager = B.nvfp4_gemm(*dev, out_dtype=torch.float32, workspace=ws).clone()
     out = torch.empty_like(eager)
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        B.nvfp4_gemm(*dev, out_dtype=torch.float32, out=out, workspace=ws)
-    torch.cuda.current_stream().wait_stream(s)
-    with torch.cuda.graph(g):
-        B.nvfp4_gemm(*dev, out_dtype=torch.float32, out=out, workspace=ws)
-    for _ in range(4):
-        out.fill_(float("nan"))
-        g.replay()
-        torch.cuda.synchronize()
-        assert torch.equal(out.view(torch.int32), eager.view(torch.int32))
+    _replays_match(lambda: B.nvfp4_gemm(*dev, out_dtype=torch.float32, out=out, workspace=ws), out, eager)
+    U.assert_within(eager.cpu().numpy(), C, T, "graph")
+
+
+def test_m16_unsplit_graph_replays():
+    """The unsplit M-tile kernel (a product with enough rows to fill the GPU: no split even with
+    a workspace) inside a replayed HIP graph."""
+    M, K, N = 16, 5120, 20000
+    assert B.gemm_dispatch(M, K, N, 1 << 24) == B.KERNEL_M16
+    assert int(B.load().nvfp4_gemm_workspace_bytes(M, K, N)) == 0
+    dev, C, T = _pair(M, K, N, 10)
+    eager = B.nvfp4_gemm(*dev, out_dtype=torch.float32).clone()
+    out = torch.empty_like(eager)
+    _replays_match(lambda: B.nvfp4_gemm(*dev, out_dtype=torch.float32, out=out), out, eager)
     U.assert_within(eager.cpu().numpy(), C, T, "graph")
 
 
