@@ -149,7 +149,63 @@ def test_gemm_empty():
 # Full-size workloads, auto path (the launch configuration the benchmark times).
 # ---------------------------------------------------------------------------
 
-def _full(name, n_sample=384, workspace="auto"):
+_FULL_ORACLE: dict = {}
+
+
+def full_oracle(name):
+    """The oracle's product of a whole workload (every output), from the seeded inputs; cached
+    for the module (the weight quantization is ~15 s per 131M-element matrix)."""
+    if name not in _FULL_ORACLE:
+        wl = WL.get(name)
+        inp = WL.generate(wl)
+        a = inp.a_f32()
+        g_a = Q.global_scale(a)
+        g_w = Q.global_scale(inp.W)
+        ap, asp = Q.quantize_packed(a, g_a)
+        C = np.empty((wl.M, wl.N))
+        T = np.empty((wl.M, wl.N))
+        for n0 in range(0, wl.N, 4096):
+            wp, wsp = Q.quantize_packed(inp.W[n0:n0 + 4096], g_w)
+            C[:, n0:n0 + 4096], T[:, n0:n0 + 4096] = G.gemm_ref(ap, asp, g_a, wp, wsp, g_w)
+        _FULL_ORACLE[name] = (wl, inp, g_a, C, T)
+    return _FULL_ORACLE[name]
+
+
+def stored_bound(C, T, out_dtype):
+    """The bound for a stored result: the GEMM tolerance, plus for a bf16 result the rounding of
+    the fp32 value v (|v - C| <= T) to bf16, at most half an ulp: 2^-8 |v| <= 2^-8 (|C| + T)."""
+    if out_dtype == torch.bfloat16:
+        return T + 2.0 ** -8 * (np.abs(C) + T)
+    return T
+
+
+@pytest.mark.parametrize("name,workspace", [("decode_up", "auto"), ("verify_down", "auto"), ("verify_down", None)])
+def test_full_size_every_output(name, workspace):
+    """Every output of the decode up-projection (1 x 5120 x 25600, FP4 GEMV) and of the tree-
+    verification down-projection (16 x 25600 x 5120, split M-tile kernel with the workspace, the
+    skinny kernel without), in the benchmark's launch configuration."""
+    wl, inp, g_a, C, T = full_oracle(name)
+    wc, ws, gw = B.nvfp4_quantize_weights(U.dev_f32(inp.W))
+    ac, asc = B.nvfp4_quantize_act(U.dev_acts(inp), U.scalar(g_a))
+    out_dtype = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
+    out = U.host(B.nvfp4_gemm(ac, asc, U.scalar(g_a), wc, ws, gw, out_dtype=out_dtype, workspace=workspace))
+    print(f"{name}: {int(np.sum(np.abs(out - C) > T))} of {C.size} outputs need the bf16 rounding allowance")
+    U.assert_within(out, C, stored_bound(C, T, out_dtype), f"{name} workspace={workspace}")
+
+
+def test_full_size_decode_fused_every_output():
+    """The decode step as the benchmark runs it: nvfp4_quantize_gemm (activation quantization
+    inside the FP4 GEMV, one kernel) on the raw bf16 row; every output, and the activation codes
+    and scales bit-exact."""
+    wl, inp, g_a, C, T = full_oracle("decode_up")
+    wc, ws, gw = B.nvfp4_quantize_weights(U.dev_f32(inp.W))
+    out, ac, asc = B.nvfp4_quantize_gemm(U.dev_acts(inp), U.scalar(g_a), wc, ws, gw, out_dtype=torch.bfloat16)
+    ap, asp = Q.quantize_packed(inp.a_f32(), g_a)
+    assert np.array_equal(ac.cpu().numpy(), ap) and np.array_equal(asc.cpu().numpy(), asp)
+    U.assert_within(U.host(out), C, stored_bound(C, T, torch.bfloat16), "decode_up fused")
+
+
+def _sampled(name, n_sample=384):
     wl = WL.get(name)
     inp = WL.generate(wl)
     a = inp.a_f32()
@@ -157,7 +213,7 @@ def _full(name, n_sample=384, workspace="auto"):
     wc, ws, gw = B.nvfp4_quantize_weights(U.dev_f32(inp.W))
     ac, asc = B.nvfp4_quantize_act(U.dev_acts(inp), U.scalar(g_a))
     out_dtype = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
-    out = U.host(B.nvfp4_gemm(ac, asc, U.scalar(g_a), wc, ws, gw, out_dtype=out_dtype, workspace=workspace))
+    out = U.host(B.nvfp4_gemm(ac, asc, U.scalar(g_a), wc, ws, gw, out_dtype=out_dtype, workspace="auto"))
     rng = np.random.default_rng(3)
     cols = np.unique(np.concatenate([[0, wl.N - 1], rng.choice(wl.N, min(n_sample, wl.N), replace=False)]))
     g_w = Q.global_scale(inp.W)
@@ -167,16 +223,12 @@ def _full(name, n_sample=384, workspace="auto"):
     return wl, out, cols, C, T
 
 
-@pytest.mark.parametrize("name,workspace", [("tiny", "auto"), ("decode_up", "auto"), ("verify_down", "auto"),
-                                            ("verify_down", None), ("lm_head", "auto")])
-def test_full_size_sampled_outputs(name, workspace):
-    """Sampled outputs at full size, in the benchmark's launch configuration (the automatic path
-    with the cached workspace), and the tree-verification down-projection without one."""
-    wl, out, cols, C, T = _full(name, workspace=workspace)
-    # precondition for the strict bound with a bf16 result: the output rounding (2^-8 |C|)
-    # must fit inside 1e-3 * sum|a*w|
-    if wl.out_dtype == "bf16":
-        assert np.all(np.abs(C) * 2.0 ** -8 <= 0.5 * T)
+@pytest.mark.parametrize("name", ["tiny", "lm_head"])
+def test_full_size_sampled_outputs(name):
+    """The tiny GEMV (every output: 256 columns) and sampled columns of the 151936-column LM head
+    (the oracle would need ~3 minutes for all of them; its argmax is checked exactly below)."""
+    wl, out, cols, C, T = _sampled(name)
+    assert wl.out_dtype == "f32"
     U.assert_within(out[:, cols], C, T, name)
 
 
@@ -201,9 +253,18 @@ def _golden_admissible():
     return [adm[m] for m in range(len(adm))]
 
 
+def fp32_accumulation_estimate(K: int, tol: float) -> float:
+    """Typical error of an fp32 sum of K exact products whose magnitudes add up to
+    S = tol / 1e-3: rounding errors of random sign, u * sqrt(K) * S with u = 2^-24."""
+    return 2.0 ** -24 * np.sqrt(K) * tol / G.REL_TOL
+
+
 def test_lm_head_argmax_matches_oracle():
-    """Per-row argmax of the full 151936-column NVFP4 LM head equals the oracle's (the tree
-    acceptance at temperature 0 compares argmax tokens)."""
+    """Per-row argmax of the full 151936-column NVFP4 LM head equals the oracle's exactly, on all
+    16 rows (the tree acceptance at temperature 0 compares argmax tokens).  The golden margins
+    make this well posed: every row's top-2 gap is more than 40 times the typical fp32
+    accumulation error of the two logits, and the GPU logits at both columns are measured to be
+    well inside half the gap."""
     wl = WL.get("lm_head")
     inp = WL.generate(wl)
     a = inp.a_f32()
@@ -217,13 +278,15 @@ def test_lm_head_argmax_matches_oracle():
     adm = _golden_admissible()
     assert len(gold) == wl.M == len(adm)
     for m, best, vbest, second, vsecond, tol in gold:
-        # the GPU decides in fp32: any column within the error bounds of the exact maximum is a
-        # correct argmax; where the oracle leaves a single such column it must be that one
-        assert int(top[m]) in adm[m], (m, int(top[m]), sorted(adm[m]), float(host[m, top[m]]), vbest)
-        if len(adm[m]) == 1:
-            assert top[m] == best
-        assert abs(host[m, best] - vbest) <= tol
-        print(f"row {m}: argmax {best} margin {vbest - vsecond:.4g} tol {tol:.3g} admissible {len(adm[m])}")
+        gap = vbest - vsecond
+        est = fp32_accumulation_estimate(wl.K, tol)
+        assert gap > 40 * 2 * est, (m, gap, est)  # the seed gives no near-tie
+        err_b, err_s = abs(host[m, best] - vbest), abs(host[m, second] - vsecond)
+        print(f"row {m}: argmax {best} gap {gap:.4g} fp32 estimate {est:.3g} measured errors "
+              f"{err_b:.3g} {err_s:.3g} tol {tol:.3g} admissible set {sorted(adm[m])}")
+        assert err_b + err_s < gap / 2, (m, err_b, err_s, gap)
+        assert err_b <= tol
+        assert int(top[m]) == best, (m, int(top[m]), best, float(host[m, top[m]]), vbest)
 
 
 def test_prefill_chain_up_then_down():
@@ -239,9 +302,9 @@ def test_prefill_chain_up_then_down():
     rng = np.random.default_rng(4)
     rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 14, replace=False)]))
     cols1 = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 126, replace=False)]))
-    cols2 = np.unique(np.concatenate([[0, K - 1], rng.choice(K, 126, replace=False)]))
 
-    # oracle: GEMM1 on the sampled rows (all columns: needs all of W1), GEMM2 on sampled columns
+    # oracle: GEMM1 on the sampled rows (all columns: needs all of W1) and on sampled columns,
+    # GEMM2 on every column of the sampled rows
     gw1 = Q.global_scale(inp.W)
     gw2 = Q.global_scale(inp.W2)
     ap, asp = Q.quantize_packed(a, g1)
@@ -252,8 +315,11 @@ def test_prefill_chain_up_then_down():
     y1r = WL.bf16_bits_to_f32(y1r_bits)
     g2 = Q.global_scale(y1r)
     a2p, a2s = Q.quantize_packed(y1r, g2)
-    w2p, w2s = Q.quantize_packed(inp.W2[cols2], gw2)
-    C2, T2 = G.gemm_ref(a2p, a2s, g2, w2p, w2s, gw2)
+    C2 = np.empty((len(rows), K))
+    T2 = np.empty((len(rows), K))
+    for k0 in range(0, K, 1024):
+        w2p, w2s = Q.quantize_packed(inp.W2[k0:k0 + 1024], gw2)
+        C2[:, k0:k0 + 1024], T2[:, k0:k0 + 1024] = G.gemm_ref(a2p, a2s, g2, w2p, w2s, gw2)
 
     # GPU chain, exactly as the benchmark runs it
     wc1, ws1, gw1_d = B.nvfp4_quantize_weights(U.dev_f32(inp.W))
@@ -267,8 +333,8 @@ def test_prefill_chain_up_then_down():
     assert torch.equal(qc, ac2) and torch.equal(qs, as2)
 
     y1h = U.host(y1)
-    U.assert_within(y1h[rows], C1r, T1r, "GEMM1 sampled rows")
-    U.assert_within(y1h[:, cols1], C1c, T1c, "GEMM1 sampled columns")
+    U.assert_within(y1h[rows], C1r, stored_bound(C1r, T1r, torch.bfloat16), "GEMM1 sampled rows")
+    U.assert_within(y1h[:, cols1], C1c, stored_bound(C1c, T1c, torch.bfloat16), "GEMM1 sampled columns")
     # Re-quantization: a block's codes are compared where both sides fed it the same 16 bf16
     # values (the fp32-accumulated GPU Y1 and the fp64 oracle Y1 round to bf16 identically
     # almost everywhere); such blocks must match bit for bit, and mismatched inputs must be rare.
@@ -279,4 +345,4 @@ def test_prefill_chain_up_then_down():
     gs = as2[torch.as_tensor(rows, device=y1.device)].cpu().numpy()
     assert np.array_equal(gs[same], a2s[same])
     assert np.array_equal(gc[same], a2p.reshape(len(rows), N // 16, 8)[same])
-    U.assert_within(U.host(y2)[np.ix_(rows, cols2)], C2, T2, "GEMM2 sampled rows x columns")
+    U.assert_within(U.host(y2)[rows], C2, stored_bound(C2, T2, torch.bfloat16), "GEMM2 sampled rows, every column")
