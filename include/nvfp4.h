@@ -73,7 +73,9 @@ typedef enum {
   NVFP4_ERR_SHAPE = 2,  /* negative size, K < 16, K % 16 != 0, or too large      */
   NVFP4_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned                      */
   NVFP4_ERR_DTYPE = 4,  /* unsupported dtype or path selector                    */
-  NVFP4_ERR_HIP = 5     /* the HIP runtime rejected a launch                     */
+  NVFP4_ERR_HIP = 5,    /* the HIP runtime rejected a launch                     */
+  NVFP4_ERR_SCRATCH = 6 /* nvfp4_gemm_scratch: the product needs more workspace
+                           than the fixed scratch holds                        */
 } nvfp4_status;
 
 typedef enum {
@@ -205,6 +207,33 @@ nvfp4_status nvfp4_gemm_ws(int64_t M, int64_t K, int64_t N,
                            const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
                            void* out, nvfp4_dtype out_dt, void* workspace, int64_t workspace_bytes,
                            void* stream);
+
+/* Size in bytes of the fixed per-device scratch array of nvfp4_gemm_scratch. */
+#define NVFP4_SCRATCH_BYTES 4194304
+
+/* nvfp4_gemm_ws for callers that cannot allocate or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The split-K workspace is a fixed device array inside the
+ * library, NVFP4_SCRATCH_BYTES (4 MiB) per device, held until the process
+ * ends; the call allocates nothing.  Same arguments and result contract as
+ * nvfp4_gemm, and bit-identical to nvfp4_gemm_ws with a large enough
+ * workspace (the same kernels and split plan).
+ *   - A product whose nvfp4_gemm_workspace_bytes exceeds NVFP4_SCRATCH_BYTES
+ *     is rejected with NVFP4_ERR_SCRATCH, enqueuing nothing (on a 256-CU
+ *     MI355X no split plan needs more than about 2 MiB).
+ *   - Every call on a device shares that device's array and leaves its
+ *     counters zero for the next: calls that overlap on one GPU (on different
+ *     streams, or graph replays running concurrently) race and may produce
+ *     wrong results.  Keep them ordered on one stream.
+ *   - The first call on a device takes the array's device address and
+ *     enqueues, on `stream`, a small kernel that clears its counter area
+ *     (also when that call is being captured into a graph).
+ * Validation as nvfp4_gemm; NVFP4_ERR_HIP if the array's address cannot be
+ * taken. */
+nvfp4_status nvfp4_gemm_scratch(int64_t M, int64_t K, int64_t N,
+                                const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                                const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                                void* out, nvfp4_dtype out_dt, void* stream);
 
 /* NVFP4 W4A4 GEMM whose output is also emitted in NVFP4: the product of one
  * layer of a prefill becomes the quantized activations of the next.

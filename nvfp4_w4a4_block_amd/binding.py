@@ -18,7 +18,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
 
-NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_DTYPE, NVFP4_ERR_HIP = range(6)
+NVFP4_OK, NVFP4_ERR_NULL, NVFP4_ERR_SHAPE, NVFP4_ERR_ALIGN, NVFP4_ERR_DTYPE, NVFP4_ERR_HIP, NVFP4_ERR_SCRATCH = range(7)
+SCRATCH_BYTES = 4 << 20  # NVFP4_SCRATCH_BYTES
 NVFP4_F32, NVFP4_BF16 = 0, 1
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 # kernel selectors of nvfp4_gemm_ex (and values of nvfp4_gemm_dispatch)
@@ -29,7 +30,7 @@ KERNEL_NAMES = {KERNEL_GEMV_FP4: "gemv_fp4_kernel", KERNEL_GEMV_FLAT: "gemv_flat
                 KERNEL_TILED_PERSISTENT: "gemm_wg_tiled_kernel", KERNEL_TILED: "gemm_tiled_kernel"}
 
 EXPORTS = ("nvfp4_abi_version", "nvfp4_act_global_scale", "nvfp4_gemm", "nvfp4_gemm_dispatch", "nvfp4_gemm_ex",
-           "nvfp4_gemm_quantize_output", "nvfp4_gemm_workspace_bytes", "nvfp4_gemm_ws", "nvfp4_kv_fp8_decode", "nvfp4_kv_fp8_encode",
+           "nvfp4_gemm_quantize_output", "nvfp4_gemm_scratch", "nvfp4_gemm_workspace_bytes", "nvfp4_gemm_ws", "nvfp4_kv_fp8_decode", "nvfp4_kv_fp8_encode",
            "nvfp4_quantize_act",
            "nvfp4_quantize_gemm", "nvfp4_quantize_gemm_dynamic", "nvfp4_quantize_weights", "nvfp4_status_string",
            "nvfp4_stream_read",
@@ -59,6 +60,7 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_gemm.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, p]
     lib.nvfp4_gemm_ex.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, i32, p]
     lib.nvfp4_gemm_ws.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, p, i64, p]
+    lib.nvfp4_gemm_scratch.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, p]
     lib.nvfp4_gemm_quantize_output.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, i32, p, p, p, p]
     lib.nvfp4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
     lib.nvfp4_gemm_workspace_bytes.restype = i64
@@ -73,6 +75,7 @@ def load() -> ctypes.CDLL:
     lib.nvfp4_kv_fp8_decode.argtypes = [p, i64, p, p, i32, p]
     lib.nvfp4_tree_verify.argtypes = [i64, i64, i64, p, p, p, p, p, p, p, p, p, p, p, p, p]
     for f in ("nvfp4_quantize_weights", "nvfp4_quantize_act", "nvfp4_gemm", "nvfp4_gemm_ex", "nvfp4_gemm_ws",
+              "nvfp4_gemm_scratch",
               "nvfp4_gemm_quantize_output",
               "nvfp4_quantize_gemm", "nvfp4_tree_accept", "nvfp4_tree_verify", "nvfp4_kv_fp8_encode",
               "nvfp4_kv_fp8_decode", "nvfp4_act_global_scale", "nvfp4_stream_read"):

@@ -32,6 +32,7 @@ SOURCES = {
     "kv_fp8.hip": [],
     "gemm_tiled.hip": [],
     "stream.hip": [],
+    "scratch.hip": [],
     "abi.cpp": [],
 }
 

@@ -37,11 +37,12 @@ const char* nvfp4_status_string(nvfp4_status s) {
     case NVFP4_ERR_ALIGN: return "pointer not aligned (arrays: 16 bytes, scalars: 4 bytes)";
     case NVFP4_ERR_DTYPE: return "unsupported dtype or path";
     case NVFP4_ERR_HIP: return "HIP runtime error while launching";
+    case NVFP4_ERR_SCRATCH: return "the product needs more split-K workspace than the fixed scratch holds";
   }
   return "unknown status";
 }
 
-int nvfp4_abi_version(void) { return 9; }
+int nvfp4_abi_version(void) { return 10; }
 
 nvfp4_status nvfp4_quantize_weights(const void* w, nvfp4_dtype w_dt, int64_t N, int64_t K,
                                     uint8_t* w_codes, uint8_t* w_scales, float* w_global,
@@ -125,7 +126,7 @@ hipError_t launch_path(int path, const nvfp4::GemmArgs& g, hipStream_t s) {
   }
 }
 
-// Validation of nvfp4_gemm_ex / nvfp4_gemm_ws; on success
+// Validation of nvfp4_gemm_ex / nvfp4_gemm_ws / nvfp4_gemm_scratch; on success
 // *path is the resolved path or kernel and *g the arguments (g->M == 0 or
 // g->N == 0: nothing to run).
 nvfp4_status gemm_validate(int64_t M, int64_t K, int64_t N,
@@ -219,6 +220,28 @@ nvfp4_status nvfp4_gemm_ws(int64_t M, int64_t K, int64_t N,
                            void* stream) {
   return gemm_impl(M, K, N, a_codes, a_scales, a_global, w_codes, w_scales, w_global, out, out_dt,
                    NVFP4_PATH_AUTO, workspace, workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_gemm_scratch(int64_t M, int64_t K, int64_t N,
+                                const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                                const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                                void* out, nvfp4_dtype out_dt, void* stream) {
+  int path = NVFP4_PATH_AUTO;
+  nvfp4::GemmArgs g;
+  nvfp4_status st = gemm_validate(M, K, N, a_codes, a_scales, a_global, w_codes, w_scales, w_global, out, out_dt,
+                                  &path, nullptr, 0, &g);
+  if (st != NVFP4_OK || g.M == 0 || g.N == 0) return st;
+  const int64_t need = nvfp4_gemm_workspace_bytes(M, K, N);
+  if (need > nvfp4::kScratchBytes) return NVFP4_ERR_SCRATCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (need > 0) {
+    void* ws = nullptr;
+    const hipError_t e = nvfp4::scratch_workspace(&ws, s);
+    if (e != hipSuccess) return NVFP4_ERR_HIP;
+    g.workspace = ws;
+    g.workspace_bytes = nvfp4::kScratchBytes;
+  }
+  return from_hip(launch_path(path, g, s));
 }
 
 nvfp4_status nvfp4_gemm_quantize_output(int64_t M, int64_t K, int64_t N,

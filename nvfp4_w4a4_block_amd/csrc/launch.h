@@ -125,6 +125,13 @@ hipError_t launch_gemm_tiled_simple(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
 bool gemm_tiled_quant_out_supported(const GemmArgs& a);
 
+// Fixed device scratch (scratch.hip) for callers that cannot allocate: the
+// size of the per-device array (NVFP4_SCRATCH_BYTES in include/nvfp4.h), and
+// the current device's address of it (taken once per device, when its counter
+// area is also cleared by a kernel on `stream`).
+constexpr int64_t kScratchBytes = (int64_t)4 << 20;
+hipError_t scratch_workspace(void** out, hipStream_t stream);
+
 // Read-only stream over two arrays (stream.hip): the measured read ceiling
 // of a weight matrix's codes and scales.  sink[0] is written only if the XOR
 // of everything read equals `magic`.

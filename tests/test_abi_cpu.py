@@ -39,10 +39,10 @@ def test_exported_symbols_are_c_linkage():
 
 
 def test_status_strings_and_version(lib):
-    for s in range(6):
-        assert B.status_string(s)
+    for s in range(7):
+        assert B.status_string(s) and B.status_string(s) != "unknown status"
     assert B.status_string(99) == "unknown status"
-    assert lib.nvfp4_abi_version() == 9
+    assert lib.nvfp4_abi_version() == 10
 
 
 def gemm(lib, M, K, N, ptrs=(A16,) * 7, out_dt=B.NVFP4_BF16, path=B.PATH_AUTO):
