@@ -157,40 +157,6 @@ __global__ __launch_bounds__(kThreads) void gemm_m16_kernel(GemmArgs p, int LS, 
   };
 
   u4_t sX = {0u, 0u, 0u, 0u}, sY = {0u, 0u, 0u, 0u};
-  if constexpr (SB) {
-    // this wave's 16 rows x lines [l0, l0 + Lr) of scale bytes: chunk c of row
-    // r (16 bytes, lines 2c and 2c + 1) -> slot row r at 16 c (as dwords)
-    const uint32_t nch = (uint32_t)(Lr + 1) >> 1, total = 16u * nch;
-    u4_t v[8];
-#pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
-      const uint32_t c = (uint32_t)lane + 64u * s8;
-      const uint32_t r = c / nch, k = c - r * nch;
-      v[s8] = __builtin_amdgcn_raw_buffer_load_b128(
-          ws, c < total ? (row0 + r) * srow + 8u * (uint32_t)l0 + 16u * k : kOOB, 0, 0);
-    }
-    uint8_t* const slot0 = lds_m16 + kARegion + (uint32_t)wave * 16u * sb_stride(LS);
-#pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
-      const uint32_t c = (uint32_t)lane + 64u * s8;
-      const uint32_t r = c / nch, k = c - r * nch;
-      if (c < total) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(slot0 + r * sb_stride(LS) + 16u * k + 4u * i) = v[s8][i];
-      }
-    }
-  } else {
-    sX = load_scales(0);
-    sY = load_scales(4);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  Pair buf[kD];
-#pragma unroll
-  for (int d = 0; d < kD; ++d) {
-    buf[d] = load(d);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
   // Thread i dequantizes 16-element block i of each window: row i / 32,
   // block i % 32 (line (i % 32) / 8 of the window, block i % 8 of that line).
   const uint32_t aw_r = threadIdx.x >> 5, aw_b = threadIdx.x & 31;
@@ -209,7 +175,48 @@ __global__ __launch_bounds__(kThreads) void gemm_m16_kernel(GemmArgs p, int LS, 
     *reinterpret_cast<h8_t*>(dst) = dequant8(aw_c.x, sc);
     *reinterpret_cast<h8_t*>(dst + 16) = dequant8(aw_c.y, sc);
   };
+  // Set-up in one memory round trip: the weight scales (or the first two
+  // 8-line scale blocks), the first activation window and the first weight
+  // loads are all requested before anything waits; the scale staging and the
+  // window store then wait only for their own loads, which are earlier in the
+  // in-order load counter (measured: the K-split down-projection 4.7% faster,
+  // the LM head unchanged).
+  u4_t sbv[8];
+  [[maybe_unused]] const uint32_t nch = (uint32_t)(Lr + 1) >> 1, total = 16u * nch;
+  if constexpr (SB) {
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const uint32_t c = (uint32_t)lane + 64u * s8;
+      const uint32_t r = c / nch, k = c - r * nch;
+      sbv[s8] = __builtin_amdgcn_raw_buffer_load_b128(
+          ws, c < total ? (row0 + r) * srow + 8u * (uint32_t)l0 + 16u * k : kOOB, 0, 0);
+    }
+  } else {
+    sX = load_scales(0);
+    sY = load_scales(4);
+  }
   aw_load(0);
+  __builtin_amdgcn_sched_barrier(0);
+  Pair buf[kD];
+#pragma unroll
+  for (int d = 0; d < kD; ++d) {
+    buf[d] = load(d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (SB) {
+    // this wave's 16 rows x lines [l0, l0 + Lr) of scale bytes: chunk c of row
+    // r (16 bytes, lines 2c and 2c + 1) -> slot row r at 16 c (as dwords)
+    uint8_t* const slot0 = lds_m16 + kARegion + (uint32_t)wave * 16u * sb_stride(LS);
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const uint32_t c = (uint32_t)lane + 64u * s8;
+      const uint32_t r = c / nch, k = c - r * nch;
+      if (c < total) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(slot0 + r * sb_stride(LS) + 16u * k + 4u * i) = sbv[s8][i];
+      }
+    }
+  }
   aw_store(0);
   aw_load(1);
   barrier_lds();

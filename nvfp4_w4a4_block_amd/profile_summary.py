@@ -4,6 +4,8 @@
         --title TEXT --command TEXT [--bytes B | --flops F [--peak-tflops P]] [--kernel SUBSTR]
     python -m nvfp4_w4a4_block_amd.profile_summary traffic <fetch.csv> <write.csv> <out.json> \
         --kernel SUBSTR --sources FILE... --command TEXT --command TEXT [--copy-mib 128]
+    python -m nvfp4_w4a4_block_amd.profile_summary counters <pass.csv>... <out.md> \
+        --title TEXT --command TEXT... --kernel SUBSTR=LABEL... [--cus 256]
 
 `trace` turns the per-kernel statistics of `rocprofv3 --kernel-trace --stats
 --output-format csv` into a markdown table (and, with --bytes, the achieved
@@ -14,6 +16,11 @@ peak).  `traffic` reads two `rocprofv3 --pmc FETCH_SIZE`
 of known size (the last three copy dispatches), and writes the HBM bytes per
 launch of the named kernel together with a SHA-256 of the kernel's sources;
 bench.py reports the figure only while those sources are unchanged.
+`counters` merges the `rocprofv3 --pmc` counter files of several passes over
+the same command (one pass per counter set, since one pass holds at most
+eight SQ counters), averages each counter over the dispatches of each named
+kernel, and derives the matrix-core busy fraction, the instruction mix per
+MFMA, the LDS bank-conflict share and the share of wave time spent waiting.
 """
 from __future__ import annotations
 
@@ -104,6 +111,72 @@ def traffic(args) -> None:
         f.write("\n")
 
 
+def _ratio(d, num, den, scale=1.0):
+    if num in d and den in d and d[den]:
+        return scale * d[num] / d[den]
+    return None
+
+
+def counters(args) -> None:
+    labels = [kv.split("=", 1) for kv in args.kernel]
+    per = {lab: {} for _, lab in labels}
+    n_disp = {lab: {} for _, lab in labels}
+    dur = {lab: [] for _, lab in labels}
+    for path in args.passes:
+        vals = {lab: {} for _, lab in labels}
+        for r in csv.DictReader(open(path)):
+            for sub, lab in labels:
+                if sub in r["Kernel_Name"]:
+                    vals[lab].setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                    if r["Counter_Name"] == next(iter(vals[lab])):
+                        dur[lab].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        for lab, d in vals.items():
+            for c, v in d.items():
+                per[lab][c] = statistics.mean(v)
+                n_disp[lab][c] = len(v)
+    cus, simds = args.cus, 4 * args.cus
+    out = [f"# {args.title}", "", "Commands (one pass per counter set; repository root, MI355X):", ""]
+    out += ["```", *args.command, "```", ""]
+    for sub, lab in labels:
+        d = per[lab]
+        if not d:
+            sys.exit(f"no dispatches of {sub!r}")
+        out += [f"## {lab}", "", f"Kernel: `{sub}`; mean over {min(n_disp[lab].values())} to "
+                f"{max(n_disp[lab].values())} dispatches per counter; mean dispatch duration under the "
+                f"counter passes {statistics.mean(dur[lab]) / 1e3:.1f} us.", ""]
+        out += ["| Counter | Mean per dispatch |", "| :-- | --: |"]
+        out += [f"| {c} | {v:,.0f} |" for c, v in sorted(d.items())]
+        derived = []
+        busy = None
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in d and d.get("SQ_BUSY_CU_CYCLES"):
+            busy = (d["SQ_VALU_MFMA_BUSY_CYCLES"] / simds) / (d["SQ_BUSY_CU_CYCLES"] / cus)
+            derived.append(("matrix-core busy: SQ_VALU_MFMA_BUSY_CYCLES per SIMD / SQ_BUSY_CU_CYCLES per CU",
+                            f"{100 * busy:.1f}%"))
+        if "SQ_INSTS_VALU" in d and d.get("SQ_INSTS_MFMA"):
+            derived.append(("non-MFMA VALU instructions per MFMA: (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA",
+                            f"{(d['SQ_INSTS_VALU'] - d['SQ_INSTS_MFMA']) / d['SQ_INSTS_MFMA']:.2f}"))
+        for name, num in (("SALU", "SQ_INSTS_SALU"), ("LDS", "SQ_INSTS_LDS"), ("vector-memory read", "SQ_INSTS_VMEM_RD")):
+            v = _ratio(d, num, "SQ_INSTS_MFMA")
+            if v is not None:
+                derived.append((f"{name} instructions per MFMA: {num} / SQ_INSTS_MFMA", f"{v:.2f}"))
+        v = _ratio(d, "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CU_CYCLES", 100)
+        if v is not None:
+            derived.append(("LDS bank-conflict cycles / CU busy cycles", f"{v:.1f}%"))
+        for num in ("SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_WAIT_INST_LDS"):
+            v = _ratio(d, num, "SQ_WAVE_CYCLES", 100)
+            if v is not None:
+                derived.append((f"{num} / SQ_WAVE_CYCLES", f"{v:.1f}%"))
+        if "SQ_INSTS_VALU_MFMA_MOPS_F16" in d:
+            derived.append(("f16 matrix flops per dispatch: 512 x SQ_INSTS_VALU_MFMA_MOPS_F16",
+                            f"{512 * d['SQ_INSTS_VALU_MFMA_MOPS_F16']:.4g}"))
+        if derived:
+            out += ["", "| Derived | Value |", "| :-- | --: |"]
+            out += [f"| {k} | {v} |" for k, v in derived]
+        out.append("")
+    with open(args.out, "w") as f:
+        f.write("\n".join(out) + "\n")
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -124,8 +197,15 @@ def main() -> None:
     r.add_argument("--sources", nargs="+", required=True)
     r.add_argument("--command", action="append", required=True)
     r.add_argument("--copy-mib", type=int, default=128)
+    c = sub.add_parser("counters")
+    c.add_argument("passes", nargs="+")
+    c.add_argument("out")
+    c.add_argument("--title", required=True)
+    c.add_argument("--command", action="append", required=True)
+    c.add_argument("--kernel", action="append", required=True, help="SUBSTR=LABEL")
+    c.add_argument("--cus", type=int, default=256)
     a = ap.parse_args()
-    trace(a) if a.cmd == "trace" else traffic(a)
+    {"trace": trace, "traffic": traffic, "counters": counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
