@@ -102,7 +102,10 @@ typedef enum {
   NVFP4_KERNEL_SKINNY16 = 7,          /* skinny kernel, any K, any M              */
   NVFP4_KERNEL_TILED_PERSISTENT = 8,  /* persistent 64x160-tile MFMA kernel,
                                          K % 1024 == 0                            */
-  NVFP4_KERNEL_TILED = 9              /* 128x128-tile MFMA kernel, any shape      */
+  NVFP4_KERNEL_TILED = 9,             /* 128x128-tile MFMA kernel, any shape      */
+  NVFP4_KERNEL_M16_STREAM = 10        /* persistent weight stream on f16 matrix
+                                         cores: M <= 16, K % 1024 == 0 (or a
+                                         multiple of 1536, 2048 or 2560)          */
 } nvfp4_path;
 
 /* Offline weight quantization (post-training, done once).

@@ -24,10 +24,11 @@ NVFP4_F32, NVFP4_BF16 = 0, 1
 PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
 # kernel selectors of nvfp4_gemm_ex (and values of nvfp4_gemm_dispatch)
 (KERNEL_GEMV_FP4, KERNEL_GEMV_FLAT, KERNEL_M16, KERNEL_SKINNY256, KERNEL_SKINNY16,
- KERNEL_TILED_PERSISTENT, KERNEL_TILED) = range(3, 10)
+ KERNEL_TILED_PERSISTENT, KERNEL_TILED, KERNEL_M16_STREAM) = range(3, 11)
 KERNEL_NAMES = {KERNEL_GEMV_FP4: "gemv_fp4_kernel", KERNEL_GEMV_FLAT: "gemv_flat_kernel", KERNEL_M16: "gemm_m16_kernel",
                 KERNEL_SKINNY256: "gemm_skinny256_kernel", KERNEL_SKINNY16: "gemm_skinny_kernel",
-                KERNEL_TILED_PERSISTENT: "gemm_wg_tiled_kernel", KERNEL_TILED: "gemm_tiled_kernel"}
+                KERNEL_TILED_PERSISTENT: "gemm_wg_tiled_kernel", KERNEL_TILED: "gemm_tiled_kernel",
+                KERNEL_M16_STREAM: "gemm_m16_stream_kernel"}
 
 EXPORTS = ("nvfp4_abi_version", "nvfp4_act_global_scale", "nvfp4_gemm", "nvfp4_gemm_dispatch", "nvfp4_gemm_ex",
            "nvfp4_gemm_quantize_output", "nvfp4_gemm_scratch", "nvfp4_gemm_workspace_bytes", "nvfp4_gemm_ws", "nvfp4_kv_fp8_decode", "nvfp4_kv_fp8_encode",

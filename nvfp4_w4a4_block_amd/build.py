@@ -28,6 +28,7 @@ SOURCES = {
     "gemm_skinny.hip": [],
     "gemv_fp4.hip": [],
     "gemm_m16.hip": [],
+    "gemm_m16_stream.hip": [],
     "tree.hip": [],
     "kv_fp8.hip": [],
     "gemm_tiled.hip": [],

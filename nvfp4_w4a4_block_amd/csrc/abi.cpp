@@ -42,7 +42,7 @@ const char* nvfp4_status_string(nvfp4_status s) {
   return "unknown status";
 }
 
-int nvfp4_abi_version(void) { return 10; }
+int nvfp4_abi_version(void) { return 11; }
 
 nvfp4_status nvfp4_quantize_weights(const void* w, nvfp4_dtype w_dt, int64_t N, int64_t K,
                                     uint8_t* w_codes, uint8_t* w_scales, float* w_global,
@@ -92,7 +92,7 @@ nvfp4_status nvfp4_quantize_act(const void* a, nvfp4_dtype a_dt, int64_t M, int6
 
 namespace {
 
-bool path_ok(int path) { return path >= NVFP4_PATH_AUTO && path <= NVFP4_KERNEL_TILED; }
+bool path_ok(int path) { return path >= NVFP4_PATH_AUTO && path <= NVFP4_KERNEL_M16_STREAM; }
 
 // Grid rows a path launches for M activation rows (grid.y is at most 65535).
 int64_t grid_rows(int path, int64_t M) {
@@ -106,6 +106,7 @@ bool kernel_takes(int k, const nvfp4::GemmArgs& g) {
     case NVFP4_KERNEL_GEMV_FP4: return nvfp4::gemv_fp4_supported(g);
     case NVFP4_KERNEL_GEMV_FLAT: return nvfp4::gemv_flat_supported(g);
     case NVFP4_KERNEL_M16: return nvfp4::gemm_m16_supported(g);
+    case NVFP4_KERNEL_M16_STREAM: return nvfp4::gemm_m16_stream_supported(g);
     case NVFP4_KERNEL_SKINNY256: return g.K % 256 == 0;
     case NVFP4_KERNEL_TILED_PERSISTENT: return nvfp4::gemm_tiled_persistent_supported(g);
     default: return true;  // the skinny16 and simple tiled kernels take any shape
@@ -119,6 +120,7 @@ hipError_t launch_path(int path, const nvfp4::GemmArgs& g, hipStream_t s) {
     case NVFP4_KERNEL_GEMV_FP4: return nvfp4::launch_gemv_fp4(g, s);
     case NVFP4_KERNEL_GEMV_FLAT: return nvfp4::launch_gemv_flat(g, s);
     case NVFP4_KERNEL_M16: return nvfp4::launch_gemm_m16(g, s);
+    case NVFP4_KERNEL_M16_STREAM: return nvfp4::launch_gemm_m16_stream(g, s);
     case NVFP4_KERNEL_SKINNY256: return nvfp4::launch_gemm_skinny256(g, s);
     case NVFP4_KERNEL_SKINNY16: return nvfp4::launch_gemm_skinny16(g, s);
     case NVFP4_KERNEL_TILED_PERSISTENT: return nvfp4::launch_gemm_tiled_persistent(g, s);
@@ -430,7 +432,7 @@ nvfp4_status nvfp4_tree_verify(int64_t M, int64_t K, int64_t N,
   hipError_t e;
   if (fused) {
     g.argmax_keys = keys;
-    e = nvfp4::launch_gemm_m16(g, s);
+    e = nvfp4::gemm_m16_stream_preferred(g) ? nvfp4::launch_gemm_m16_stream(g, s) : nvfp4::launch_gemm_m16(g, s);
   } else {
     e = nvfp4::launch_gemm_skinny(g, s);
     if (e == hipSuccess) e = nvfp4::launch_argmax_rows(logits, (int)M, (int)N, keys, s);

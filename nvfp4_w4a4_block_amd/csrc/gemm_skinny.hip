@@ -742,11 +742,13 @@ hipError_t launch_gemm_skinny16(const GemmArgs& a, hipStream_t stream) {
 }
 
 // The weight-streaming path's kernel for a product: the FP4 GEMV (one or two
-// rows, K a multiple of 1024 up to 8192), the M-tile kernel (3..16 rows where
-// it is faster: long K, or many rows), the memory-order GEMV (one or two rows,
-// other K from 2048 on), else the skinny kernels.
+// rows, K a multiple of 1024 up to 8192), the persistent M=16 stream (3..16
+// rows over a tall matrix), the M-tile kernel (3..16 rows where it is faster:
+// long K, or many rows), the memory-order GEMV (one or two rows, other K from
+// 2048 on), else the skinny kernels.
 int skinny_kernel_choice(const GemmArgs& a) {
   if (gemv_fp4_supported(a)) return kKernelGemvFp4;
+  if (gemm_m16_stream_preferred(a)) return kKernelM16Stream;
   if (gemm_m16_preferred(a)) return kKernelM16;
   if (gemv_flat_supported(a)) return kKernelGemvFlat;
   return a.K % 256 == 0 ? kKernelSkinny256 : kKernelSkinny16;
@@ -756,6 +758,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   switch (skinny_kernel_choice(a)) {
     case kKernelGemvFp4: return launch_gemv_fp4(a, stream);
     case kKernelM16: return launch_gemm_m16(a, stream);
+    case kKernelM16Stream: return launch_gemm_m16_stream(a, stream);
     case kKernelGemvFlat: return launch_gemv_flat(a, stream);
     case kKernelSkinny256: return launch_gemm_skinny256(a, stream);
     default: return launch_gemm_skinny16(a, stream);

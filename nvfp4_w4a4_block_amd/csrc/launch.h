@@ -84,6 +84,7 @@ enum KernelId : int {
   kKernelSkinny16 = 7,         // gemm_skinny_kernel: any K, any M
   kKernelTiledPersistent = 8,  // gemm_wg_tiled_kernel: K % 1024 == 0
   kKernelTiled = 9,            // gemm_tiled_kernel: any shape
+  kKernelM16Stream = 10,       // gemm_m16_stream_kernel: persistent weight stream, M <= 16, tall N
 };
 
 // Weight-streaming path (built for M <= 16; the skinny kernels tile larger M
@@ -113,6 +114,15 @@ bool gemm_m16_small_prefers_skinny(const GemmArgs& a);  // the skinny kernel ser
 bool gemm_m16_preferred(const GemmArgs& a);  // 3 <= M <= 16, supported, and faster than the alternatives
 int64_t gemm_m16_workspace_bytes(const GemmArgs& a);
 hipError_t launch_gemm_m16(const GemmArgs& a, hipStream_t stream);
+
+// Persistent weight stream for 1 <= M <= 16 over a tall matrix (one
+// workgroup per CU, K walked in chunks of 8-20 lines: K a multiple of 1024,
+// 1536, 2048 or 2560; N * K / 2 < 2^31).  Preferred (M >= 3) from 2 x 8 x
+// CUs groups of 16 rows on; never splits K.  Takes argmax_keys like the
+// M-tile kernel.
+bool gemm_m16_stream_supported(const GemmArgs& a);
+bool gemm_m16_stream_preferred(const GemmArgs& a);
+hipError_t launch_gemm_m16_stream(const GemmArgs& a, hipStream_t stream);
 
 // LDS-tiled MFMA path for large M: the persistent kernel where
 // gemm_tiled_persistent_supported() holds (K % 1024 == 0), else the simple

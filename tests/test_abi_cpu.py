@@ -42,7 +42,7 @@ def test_status_strings_and_version(lib):
     for s in range(7):
         assert B.status_string(s) and B.status_string(s) != "unknown status"
     assert B.status_string(99) == "unknown status"
-    assert lib.nvfp4_abi_version() == 10
+    assert lib.nvfp4_abi_version() == 11
 
 
 def gemm(lib, M, K, N, ptrs=(A16,) * 7, out_dt=B.NVFP4_BF16, path=B.PATH_AUTO):
@@ -71,7 +71,7 @@ def test_gemm_rejects_null_align_dtype_path(lib):
     # scalar scale pointers only need 4-byte alignment: this one passes validation up to the
     # dtype check, which fails first here
     assert gemm(lib, 1, 32, 16, ptrs=(A16,) * 2 + (A16 + 4,) + (A16,) * 4, out_dt=7) == B.NVFP4_ERR_DTYPE
-    assert gemm(lib, 1, 32, 16, path=10) == B.NVFP4_ERR_DTYPE
+    assert gemm(lib, 1, 32, 16, path=11) == B.NVFP4_ERR_DTYPE
     assert gemm(lib, 1, 32, 16, path=-1) == B.NVFP4_ERR_DTYPE
 
 
@@ -83,6 +83,8 @@ def test_gemm_kernel_selectors_refuse_shapes_they_do_not_take(lib):
     assert gemm(lib, 1, 32, 16, path=B.KERNEL_GEMV_FLAT) == B.NVFP4_ERR_SHAPE     # K < 2048
     assert gemm(lib, 17, 128, 16, path=B.KERNEL_M16) == B.NVFP4_ERR_SHAPE         # M > 16
     assert gemm(lib, 4, 144, 16, path=B.KERNEL_M16) == B.NVFP4_ERR_SHAPE          # K % 128 != 0
+    assert gemm(lib, 17, 1024, 16, path=B.KERNEL_M16_STREAM) == B.NVFP4_ERR_SHAPE  # M > 16
+    assert gemm(lib, 4, 1152, 16, path=B.KERNEL_M16_STREAM) == B.NVFP4_ERR_SHAPE   # 9 lines: no chunk length
     assert gemm(lib, 4, 144, 16, path=B.KERNEL_SKINNY256) == B.NVFP4_ERR_SHAPE    # K % 256 != 0
     assert gemm(lib, 40, 1280, 16, path=B.KERNEL_TILED_PERSISTENT) == B.NVFP4_ERR_SHAPE  # K % 1024 != 0
     assert gemm(lib, 0, 32, 16, ptrs=(0,) * 7, path=B.KERNEL_GEMV_FP4) == B.NVFP4_OK  # empty: nothing to run

@@ -50,6 +50,7 @@ AUTO = [
     ((16, 25600, 1024, False), B.KERNEL_SKINNY256), # starved and long K without a workspace
     ((16, 25600, 1024, True), B.KERNEL_M16),        # ... split with one
     ((16, 5120, 20000, False), B.KERNEL_M16),       # enough rows: unsplit
+    ((3, 1024, 65536, False), B.KERNEL_M16_STREAM), # a tall matrix: 2 groups of 16 rows per wave
     ((16, 5120, 3000, True), B.KERNEL_SKINNY256),   # short K, N <= 16384: no workspace needed
     ((7, 1040, 300, False), B.KERNEL_SKINNY16),
     ((17, 1024, 300, False), B.KERNEL_TILED_PERSISTENT),
@@ -80,6 +81,7 @@ FORCED = [
     (B.KERNEL_GEMV_FP4, (2, 3072, 515), (3, 3072, 515)),
     (B.KERNEL_GEMV_FLAT, (1, 4352, 1001), (1, 1024, 100)),
     (B.KERNEL_M16, (13, 1152, 257), (17, 1152, 257)),
+    (B.KERNEL_M16_STREAM, (13, 2560, 1000), (4, 1152, 257)),
     (B.KERNEL_SKINNY256, (33, 768, 129), (4, 784, 129)),
     (B.KERNEL_SKINNY16, (20, 784, 129), None),
     (B.KERNEL_TILED_PERSISTENT, (40, 2048, 170), (40, 1280, 170)),

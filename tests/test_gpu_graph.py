@@ -13,7 +13,7 @@ from oracle import quant as Q
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 5120, 2048), (16, 2560, 1024), (160, 1024, 384)])
+@pytest.mark.parametrize("M,K,N", [(1, 5120, 2048), (16, 2560, 1024), (16, 5120, 70000), (160, 1024, 384)])
 def test_graph_replays_match_eager(M, K, N):
     U.require_gpu_lib()
     inp = WL.generate(WL.get("decode_up"), M=M, K=K, N=N)
@@ -86,12 +86,14 @@ def test_dynamic_scale_step_graph_replays(M, K, N):
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {r} differs"
 
 
-def test_tree_verify_graph_replays():
-    """The LM head with the fused argmax and the acceptance kernel inside a replayed HIP graph:
-    the argmax key slots return to zero after every call, so every replay reproduces the eager
-    greedy tokens and acceptance (with eager work between replays)."""
+@pytest.mark.parametrize("N", [20000, 70000])
+def test_tree_verify_graph_replays(N):
+    """The LM head with the fused argmax and the acceptance kernel inside a replayed HIP graph
+    (20000 rows: the M-tile kernel; 70000: the persistent stream): the argmax key slots return
+    to zero after every call, so every replay reproduces the eager greedy tokens and acceptance
+    (with eager work between replays)."""
     U.require_gpu_lib()
-    M, K, N = 16, 5120, 20000
+    M, K = 16, 5120
     inp = WL.generate(WL.get("lm_head"), M=M, K=K, N=N)
     g_a = U.scalar(Q.global_scale(inp.a_f32()))
     wc, ws, gw = B.nvfp4_quantize_weights(U.dev_f32(inp.W))
