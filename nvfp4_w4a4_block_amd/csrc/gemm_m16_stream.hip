@@ -379,10 +379,13 @@ bool gemm_m16_stream_supported(const GemmArgs& a) {
          (int64_t)a.N * (a.K / 2) < ((int64_t)1 << 31);
 }
 
-// Tall matrices: at least two 16-row groups per wave of one workgroup per CU.
+// Tall matrices: from 10 groups of 16 rows per CU on (measured on MI355X at
+// M = 16, K = 5120, against the M-tile kernel: N = 32768 20.4 vs 20.2 us,
+// 40960 29.7 vs 31.7, 49152 30.6 vs 33.1, 65536 34.8 vs 36.5, 151936 79.6
+// vs 90.5; at K = 2560, N = 65536 19.3 vs 20.4).
 bool gemm_m16_stream_preferred(const GemmArgs& a) {
   return gemm_m16_stream_supported(a) && a.M >= 3 &&
-         ((int64_t)a.N + 15) / 16 >= (int64_t)2 * kWaves * device_cus_stream();
+         ((int64_t)a.N + 15) / 16 >= (int64_t)10 * device_cus_stream();
 }
 
 hipError_t launch_gemm_m16_stream(const GemmArgs& a, hipStream_t stream) {

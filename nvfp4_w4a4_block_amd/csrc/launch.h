@@ -117,9 +117,9 @@ hipError_t launch_gemm_m16(const GemmArgs& a, hipStream_t stream);
 
 // Persistent weight stream for 1 <= M <= 16 over a tall matrix (one
 // workgroup per CU, K walked in chunks of 8-20 lines: K a multiple of 1024,
-// 1536, 2048 or 2560; N * K / 2 < 2^31).  Preferred (M >= 3) from 2 x 8 x
-// CUs groups of 16 rows on; never splits K.  Takes argmax_keys like the
-// M-tile kernel.
+// 1536, 2048 or 2560; N * K / 2 < 2^31).  Preferred (M >= 3) from 10 groups
+// of 16 rows per CU on; never splits K.  Takes argmax_keys like the M-tile
+// kernel.
 bool gemm_m16_stream_supported(const GemmArgs& a);
 bool gemm_m16_stream_preferred(const GemmArgs& a);
 hipError_t launch_gemm_m16_stream(const GemmArgs& a, hipStream_t stream);
