@@ -47,6 +47,15 @@ def trace(args) -> None:
     rows = list(csv.DictReader(open(args.stats)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     out = [f"# {args.title}", "", "Command (repository root, MI355X):", "", "```", args.command, "```", ""]
+    if args.bench_json:
+        # the benchmark's own line from the profiled process: its HIP-event timings of the
+        # same launches the trace below records
+        with open(args.bench_json) as f:
+            rec = json.loads([ln for ln in f if ln.startswith("{")][-1])
+        rl = rec.get("roofline", {})
+        out += [f"Same process (bench.py's HIP events over the timed region, under the profiler): "
+                f"{rec['ms_per_step'] * 1e3:,.2f} us per step, {rl.get('us_per_launch', float('nan')):,.2f} us "
+                f"per launch of `{rl.get('kernel', '?')}`.", ""]
     if args.bytes and args.kernel:
         k = [r for r in rows if args.kernel in r["Name"]]
         if k:
@@ -189,6 +198,7 @@ def main() -> None:
     t.add_argument("--flops", type=int, default=0)
     t.add_argument("--peak-tflops", type=float, default=2500.0)
     t.add_argument("--kernel", default="")
+    t.add_argument("--bench-json", default="")
     r = sub.add_parser("traffic")
     r.add_argument("fetch")
     r.add_argument("write")
