@@ -60,8 +60,12 @@ size_t fp4_lds_bytes(int MR, int K, int G) {
          (size_t)kWaves * ((size_t)G * K / 2 + (size_t)G * 8 * MR * 4);
 }
 
-// A wave owns G groups of 8 consecutive weight rows (rows past N read zeros
-// and are not stored).  K = 256 L is a template parameter: the L lines of a
+// Wave w of the W in the grid owns the contiguous run of groups of 8
+// consecutive weight rows [floor(w NG / W), floor((w + 1) NG / W)) (NG =
+// ceil(N / 8); rows past N read zeros and are not stored): the longer runs are
+// spread evenly over the grid, so every CU gets the same share; with no more
+// groups than waves, group w.  W NG < 2^32 (N <= 2^18), so 32-bit arithmetic
+// is exact.  G bounds the run length and sizes the per-wave LDS areas.  K = 256 L is a template parameter: the L lines of a
 // group are unrolled, so every load, LDS and scale offset is an immediate and
 // a line costs one weight load, three LDS reads, one MFMA per activation row
 // and the scale arithmetic.  D weight loads are in flight per wave (D divides
@@ -76,7 +80,7 @@ size_t fp4_lds_bytes(int MR, int K, int G) {
 // across the workgroup, g_a = fl32(amax / 2688), as the standalone scale
 // kernel computes it.
 template <int MR, int L, int D, bool OUT_BF16, int FUSE>
-__global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
+__global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G, uint32_t NG) {
   static_assert(L % D == 0 && D <= L, "ring depth must divide the line count");
   constexpr int K = 256 * L;
   constexpr uint32_t row_bytes = 128u * L;
@@ -86,14 +90,24 @@ __global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int N = p.N;
-  const uint32_t wsc_bytes = (uint32_t)G * 8u * srow;
+  const uint32_t wsc_bytes = (uint32_t)G * 8u * srow;  // per-wave LDS area for G groups
   u4_t* tiles = lds;                                                      // [MR][L][64]
   float* asc = reinterpret_cast<float*>(tiles + MR * L * 64);             // [MR][K/16]
   uint8_t* wsc_all = reinterpret_cast<uint8_t*>(asc + MR * (K >> 4));
   uint8_t* wsc = wsc_all + wave * wsc_bytes;                              // [8G][K/16]
   float* slots = reinterpret_cast<float*>(wsc_all + kWaves * wsc_bytes) + wave * (G * 8 * MR);
 
-  const uint32_t row0 = (uint32_t)(blockIdx.x * kWaves + wave) * 8u * (uint32_t)G;
+  const uint32_t W = gridDim.x * (uint32_t)kWaves, wv = blockIdx.x * (uint32_t)kWaves + (uint32_t)wave;
+  int g0w, Gw;  // Gw <= G
+  if (NG <= W) {  // at most one group per wave: no division
+    g0w = (int)wv;
+    Gw = wv < NG ? 1 : 0;
+  } else {
+    g0w = (int)(wv * NG / W);
+    Gw = (int)((wv + 1u) * NG / W) - g0w;
+  }
+  const uint32_t wsc_need = (uint32_t)Gw * 8u * srow;
+  const uint32_t row0 = (uint32_t)g0w * 8u;
 
   const __amdgpu_buffer_rsrc_t ac = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.ac), (short)0, (int)(MR * row_bytes), 0x00020000);
@@ -141,13 +155,13 @@ __global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
                                                           0, 0);
     }
   }
-  // This wave's weight scales: rows row0 .. row0 + 8G - 1, contiguous.
+  // This wave's weight scales: rows row0 .. row0 + 8Gw - 1, contiguous.
   u4_t sreg[kScaleLoads];
 #pragma unroll
   for (int s = 0; s < kScaleLoads; ++s) {
     const uint32_t rel = 1024u * s + 16u * lane;
     const uint32_t off = row0 * srow + rel;
-    sreg[s] = __builtin_amdgcn_raw_buffer_load_b128(ws, rel < wsc_bytes && off < (uint32_t)N * srow ? off : kOOB,
+    sreg[s] = __builtin_amdgcn_raw_buffer_load_b128(ws, rel < wsc_need && off < (uint32_t)N * srow ? off : kOOB,
                                                      0, 2);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -160,7 +174,7 @@ __global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
   auto wload = [&](uint32_t vo, int t) {
     return __builtin_amdgcn_raw_buffer_load_b128(wc, vo + 128u * t, 0, 2);
   };
-  const uint32_t vo_first = G > 0 ? b_lane + row0 * row_bytes : kOOB;
+  const uint32_t vo_first = Gw > 0 ? b_lane + row0 * row_bytes : kOOB;
   u4_t ring[D];
 #pragma unroll
   for (int t = 0; t < D; ++t) {
@@ -250,7 +264,7 @@ __global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
 #pragma unroll
   for (int s = 0; s < kScaleLoads; ++s) {
     const uint32_t rel = 1024u * s + 16u * lane;
-    if (rel < wsc_bytes) *reinterpret_cast<u4_t*>(wsc + rel) = sreg[s];
+    if (rel < wsc_need) *reinterpret_cast<u4_t*>(wsc + rel) = sreg[s];
   }
   __syncthreads();
 
@@ -293,9 +307,9 @@ __global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
   };
 
   const uint8_t* wsc_lane = wsc + (uint32_t)(j >> 1) * srow + 4u * q;
-  for (int g = 0; g < G; ++g) {
+  for (int g = 0; g < Gw; ++g) {
     const uint32_t vo_c = b_lane + (row0 + 8u * g) * row_bytes;
-    const uint32_t vo_n = g + 1 < G ? vo_c + 8u * row_bytes : kOOB;
+    const uint32_t vo_n = g + 1 < Gw ? vo_c + 8u * row_bytes : kOOB;
     const uint8_t* wsc_g = wsc_lane + 8u * srow * g;
     Ops cur = read_ops(wsc_g, 0), prev;
     f4_t dprev[MR];
@@ -333,7 +347,7 @@ __global__ __launch_bounds__(256) void gemv_fp4_kernel(GemmArgs p, int G) {
 
   // ---- epilogue: same-wave LDS ops are ordered ----
   const float gscale = (FUSE == 0 ? *p.ga : ga_used) * (*p.gw);
-  for (int idx = lane; idx < G * 8 * MR; idx += 64) {
+  for (int idx = lane; idx < Gw * 8 * MR; idx += 64) {
     const uint32_t n = row0 + (uint32_t)(idx / MR);
     const int m = idx % MR;
     if (n < (uint32_t)N) {
@@ -361,32 +375,32 @@ int device_cus() {
 }
 
 template <int MR, int L, int D, int FUSE>
-hipError_t launch_fp4(const GemmArgs& a, int G, hipStream_t stream) {
-  const int64_t waves = (a.N + 8 * G - 1) / (8 * G);
-  const dim3 grid((unsigned)((waves + kWaves - 1) / kWaves));
+hipError_t launch_fp4(const GemmArgs& a, int G, int64_t W, hipStream_t stream) {
+  const dim3 grid((unsigned)(W / kWaves));
+  const uint32_t NG = (uint32_t)(((int64_t)a.N + 7) / 8);
   const size_t lds = fp4_lds_bytes(MR, a.K, G);
-  if (a.out_bf16) gemv_fp4_kernel<MR, L, D, true, FUSE><<<grid, 64 * kWaves, lds, stream>>>(a, G);
-  else gemv_fp4_kernel<MR, L, D, false, FUSE><<<grid, 64 * kWaves, lds, stream>>>(a, G);
+  if (a.out_bf16) gemv_fp4_kernel<MR, L, D, true, FUSE><<<grid, 64 * kWaves, lds, stream>>>(a, G, NG);
+  else gemv_fp4_kernel<MR, L, D, false, FUSE><<<grid, 64 * kWaves, lds, stream>>>(a, G, NG);
   return hipGetLastError();
 }
 
 template <int MR, int L, int D>
-hipError_t launch_fp4(const GemmArgs& a, int G, hipStream_t stream) {
-  if (!a.a_raw) return launch_fp4<MR, L, D, 0>(a, G, stream);
-  return a.a_raw_bf16 ? launch_fp4<MR, L, D, 1>(a, G, stream) : launch_fp4<MR, L, D, 2>(a, G, stream);
+hipError_t launch_fp4(const GemmArgs& a, int G, int64_t W, hipStream_t stream) {
+  if (!a.a_raw) return launch_fp4<MR, L, D, 0>(a, G, W, stream);
+  return a.a_raw_bf16 ? launch_fp4<MR, L, D, 1>(a, G, W, stream) : launch_fp4<MR, L, D, 2>(a, G, W, stream);
 }
 
 template <int MR>
-hipError_t launch_fp4_k(const GemmArgs& a, int G, hipStream_t stream) {
+hipError_t launch_fp4_k(const GemmArgs& a, int G, int64_t W, hipStream_t stream) {
   switch (a.K / 256) {  // ring depth: a divisor of L near 8
-    case 4: return launch_fp4<MR, 4, 4>(a, G, stream);
-    case 8: return launch_fp4<MR, 8, 8>(a, G, stream);
-    case 12: return launch_fp4<MR, 12, 6>(a, G, stream);
-    case 16: return launch_fp4<MR, 16, 8>(a, G, stream);
-    case 20: return launch_fp4<MR, 20, 10>(a, G, stream);
-    case 24: return launch_fp4<MR, 24, 8>(a, G, stream);
-    case 28: return launch_fp4<MR, 28, 7>(a, G, stream);
-    default: return launch_fp4<MR, 32, 8>(a, G, stream);
+    case 4: return launch_fp4<MR, 4, 4>(a, G, W, stream);
+    case 8: return launch_fp4<MR, 8, 8>(a, G, W, stream);
+    case 12: return launch_fp4<MR, 12, 6>(a, G, W, stream);
+    case 16: return launch_fp4<MR, 16, 8>(a, G, W, stream);
+    case 20: return launch_fp4<MR, 20, 10>(a, G, W, stream);
+    case 24: return launch_fp4<MR, 24, 8>(a, G, W, stream);
+    case 28: return launch_fp4<MR, 28, 7>(a, G, W, stream);
+    default: return launch_fp4<MR, 32, 8>(a, G, W, stream);
   }
 }
 
@@ -394,18 +408,31 @@ hipError_t launch_fp4_k(const GemmArgs& a, int G, hipStream_t stream) {
 
 bool gemv_fp4_supported(const GemmArgs& a) {
   if (a.M < 1 || a.M > 2 || a.K % 1024 != 0 || a.K < 1024 || a.K > 8192) return false;
+  // the grid's wave count (at most the group count) times the group count
+  // stays below 2^32 (the kernel's 32-bit run arithmetic): N <= 2^18, so at
+  // most 2^15 groups of 8 rows
+  if ((int64_t)a.N > ((int64_t)1 << 18)) return false;
   return fp4_lds_bytes(a.M, a.K, 1) <= 64 * 1024;
 }
 
-// Rows per wave: about six resident waves per CU stream best (measured on
-// MI355X: fewer leave HBM idle, many more add start-up work per row); the
-// group count is bounded by the LDS and the weight-scale staging.
+// Grid: two workgroups of four waves per CU, the groups of 8 rows dealt out
+// to the waves in contiguous runs of equal length +-1, so that every CU
+// streams the same share (measured on MI355X at decode_up, 1 x 5120 x 25600:
+// 13.18-13.35 us against 13.44-13.49 us for about six waves per CU with two
+// groups each, where 144 CUs held two workgroups and 112 one; three
+// workgroups per CU 14.8 us, one of eight waves 14.0 us).  Fewer rows: one
+// group per wave, as many waves as groups.  More rows than the per-wave
+// scale staging and LDS allow: the wave count doubles until they fit.
 hipError_t launch_gemv_fp4(const GemmArgs& a, hipStream_t stream) {
-  const int64_t target_waves = (int64_t)device_cus() * 6;
-  int G = (int)((a.N + 8 * target_waves / 2) / (8 * target_waves));
-  if (G < 1) G = 1;
-  while (G > 1 && ((int64_t)G * a.K / 2 > kScaleLoads * 1024 || fp4_lds_bytes(a.M, a.K, G) > 64 * 1024)) --G;
-  return a.M == 1 ? launch_fp4_k<1>(a, G, stream) : launch_fp4_k<2>(a, G, stream);
+  const int64_t NG = ((int64_t)a.N + 7) / 8;
+  int64_t W = (int64_t)device_cus() * 2 * kWaves;
+  if (NG < W) W = (NG + kWaves - 1) / kWaves * kWaves;
+  int G = (int)((NG + W - 1) / W);
+  while (G > 1 && ((int64_t)G * a.K / 2 > kScaleLoads * 1024 || fp4_lds_bytes(a.M, a.K, G) > 64 * 1024)) {
+    W *= 2;
+    G = (int)((NG + W - 1) / W);
+  }
+  return a.M == 1 ? launch_fp4_k<1>(a, G, W, stream) : launch_fp4_k<2>(a, G, W, stream);
 }
 
 }  // namespace nvfp4
