@@ -306,8 +306,12 @@ def bench_m16(args, wl: WL.Workload, layer=None, inp=None) -> dict:
 
     step_ms = timed(step, args.steps, args.warmup)
     kern_ms = timed(product, args.steps, args.warmup)
-    kname = B.KERNEL_NAMES[kernel] + (" + fused argmax, then tree_accept_kernel" if tree else
-                                      (", K split over workgroups" if ws is not None else ""))
+    if tree:
+        kname = B.KERNEL_NAMES[kernel] + (" with fused argmax and acceptance (one launch)"
+                                          if kernel == B.KERNEL_M16_STREAM else
+                                          " + fused argmax, then tree_accept_kernel")
+    else:
+        kname = B.KERNEL_NAMES[kernel] + (", K split over workgroups" if ws is not None else "")
     log(f"[bench] {wl.name}: step {step_ms * 1e3:.2f} us, {kname} {kern_ms * 1e3:.2f} us per launch")
     step_desc = ("nvfp4_quantize_act + nvfp4_tree_verify (LM head with fused argmax, acceptance)" if tree else
                  "nvfp4_quantize_act + nvfp4_gemm" + ("_ws (split-K workspace)" if ws is not None else ""))

@@ -358,8 +358,11 @@ nvfp4_status nvfp4_tree_accept(int64_t n_nodes, const int32_t* parent, const int
  *            return (clear it once before first use; calls sharing it must be
  *            stream-ordered).
  * Deterministic: the argmax merges per-workgroup maxima with atomic maxima
- * (64 slots per row, folded by the acceptance kernel), whose result does not
- * depend on their order.
+ * (64 slots per row), whose result does not depend on their order.  The
+ * slots are folded after the product: by a small acceptance kernel, or, on
+ * the persistent weight-stream kernel, by that kernel's last workgroup to
+ * finish (found by an arrival counter kept in the last slot of the same
+ * workspace), which also runs the acceptance: one launch per call.
  * Cites: the sections on tree-based multi-token prediction (16-node tree
  * verified in one pass) and NVFP4 quantization (the LM head is NVFP4). */
 nvfp4_status nvfp4_tree_verify(int64_t M, int64_t K, int64_t N,

@@ -432,7 +432,14 @@ nvfp4_status nvfp4_tree_verify(int64_t M, int64_t K, int64_t N,
   hipError_t e;
   if (fused) {
     g.argmax_keys = keys;
-    e = nvfp4::gemm_m16_stream_preferred(g) ? nvfp4::launch_gemm_m16_stream(g, s) : nvfp4::launch_gemm_m16(g, s);
+    if (nvfp4::gemm_m16_stream_preferred(g)) {  // acceptance fused into the product's last workgroup
+      g.tree_parent = parent;
+      g.tree_draft = draft;
+      g.tree_greedy = greedy;
+      g.tree_result = result;
+      return from_hip(nvfp4::launch_gemm_m16_stream(g, s));
+    }
+    e = nvfp4::launch_gemm_m16(g, s);
   } else {
     e = nvfp4::launch_gemm_skinny(g, s);
     if (e == hipSuccess) e = nvfp4::launch_argmax_rows(logits, (int)M, (int)N, keys, s);

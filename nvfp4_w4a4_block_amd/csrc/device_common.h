@@ -139,4 +139,51 @@ __device__ __forceinline__ f4_t mfma16x16x32(h8_t a, h8_t b, f4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Greedy acceptance of a candidate tree (page "TensorRT Edge-LLM Completes
+// the MLPerf Edge Agentic Benchmark 6.4x Faster on Jetson AGX Thor", section
+// "Using tree-based multi-token prediction to accelerate LLM inference"),
+// run by one whole wave: lane v < n holds node v's parent index, draft token
+// and greedy token (n <= 64, nodes in topological order, node 0 the root).
+// Node u is accepted when its parent is and its draft equals the parent's
+// greedy token; a parent outside [0, u) rejects it.  result = [end, L,
+// bonus, path[0 .. L-1], -1 ...] (3 + n entries): the deepest accepted node
+// (lowest index on ties), its depth, its greedy token, and the nodes at depths
+// 1 .. L on the way to it.  The walk runs in node order in scalar registers,
+// reading the parent's acceptance bit, depth and greedy token across lanes.
+__device__ __forceinline__ void tree_walk_wave(int n, int32_t par, int32_t dr, int32_t gv, int32_t* result) {
+  const int t = (int)(threadIdx.x & 63);
+  uint64_t okm = 1;     // bit v: node v accepted (the root is)
+  int32_t depth_v = 0;  // lane v: depth of node v
+  int end = 0, dend = 0;
+  for (int u = 1; u < n; ++u) {
+    const int pu = __builtin_amdgcn_readlane(par, u);
+    const bool valid = pu >= 0 && pu < u;
+    const int ps = valid ? pu : 0;
+    const int d = valid ? __builtin_amdgcn_readlane(depth_v, ps) + 1 : 0;
+    depth_v = t == u ? d : depth_v;
+    const bool ok = valid && ((okm >> ps) & 1ull) &&
+                    __builtin_amdgcn_readlane(dr, u) == __builtin_amdgcn_readlane(gv, ps);
+    if (ok) {
+      okm |= 1ull << u;
+      if (d > dend) {
+        end = u;
+        dend = d;
+      }
+    }
+  }
+  // Lane i < L: the node at depth i + 1 on the root-to-end path; -1 beyond.
+  int32_t path_v = -1;
+  int u = end;
+  for (int i = dend - 1; i >= 0; --i) {
+    path_v = t == i ? u : path_v;
+    u = __builtin_amdgcn_readlane(par, u);
+  }
+  if (t == 0) {
+    result[0] = end;
+    result[1] = dend;
+    result[2] = __builtin_amdgcn_readlane(gv, end);
+  }
+  if (t < n) result[3 + t] = path_v;
+}
+
 }  // namespace nvfp4

@@ -32,7 +32,9 @@
 // fixed order (per line, alternating two accumulators; per block, added to
 // the group's sum in chunk order), so results are identical from run to run.
 // Output: the same epilogue as the M-tile kernel (x g_a g_w, bf16 or fp32,
-// and the row-argmax keys when asked).
+// and the row-argmax keys when asked).  For the verification of a candidate
+// tree the last workgroup to finish also folds the argmax keys and runs the
+// greedy acceptance (no separate launch after the product).
 #include "device_common.h"
 #include "launch.h"
 
@@ -302,8 +304,10 @@ __global__ __launch_bounds__(kThreads) void gemm_m16_stream_kernel(GemmArgs p, i
   }
   if (p.argmax_keys) {
     // rows 4q .. 4q+3 are shared by the 16 lanes of a quarter; the maximum
-    // key does not depend on the order in which waves merge theirs
-    const uint32_t slot = (uint32_t)w % kKeySlots;
+    // key does not depend on the order in which waves merge theirs.  Slot
+    // kKeySlots - 1 takes no key: its first word is the arrival counter of
+    // the fused tree acceptance.
+    const uint32_t slot = (uint32_t)w % (kKeySlots - 1);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       uint64_t b = best[e];
@@ -316,6 +320,58 @@ __global__ __launch_bounds__(kThreads) void gemm_m16_stream_kernel(GemmArgs p, i
       if (j == 0 && m < M && b != 0)
         atomicMax(reinterpret_cast<unsigned long long*>(p.argmax_keys) + slot * 16u + m, b);
     }
+  }
+
+  if (p.tree_result) {
+    // ---- fused tree acceptance, in the last workgroup to finish.  Ordering
+    // as for a split-K ticket: every thread waits for its key maxima to
+    // complete; after the barrier the ticket's thread issues an agent-scope
+    // release fence, so every key of this workgroup happens before its
+    // ticket; the last workgroup takes an agent-scope acquire fence before
+    // it reads the keys, with agent-scope loads. ----
+    static_assert(kKeySlots * 16 == 2 * kThreads, "two key words per thread");
+    __shared__ uint32_t ticket;
+    uint64_t* const keys = p.argmax_keys;
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's key maxima have completed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      uint32_t* const cnt = reinterpret_cast<uint32_t*>(keys + (kKeySlots - 1) * 16);
+      const uint32_t t = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t == gridDim.x - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      ticket = t;
+    }
+    __syncthreads();
+    if (ticket != gridDim.x - 1) return;
+    // Lane v < M of wave 0: node v's parent and draft token (requested
+    // before the fold, which they overlap).
+    const uint32_t t = threadIdx.x;
+    int32_t par = -1, dr = 0;
+    if (t < (uint32_t)M) {
+      par = p.tree_parent[t];
+      dr = p.tree_draft[t];
+    }
+    // Thread t holds words t and t + 512 (row t % 16 of slots t / 16 and
+    // t / 16 + 32; slot kKeySlots - 1 is the counter) and resets both to
+    // zero, the counter with them; rows fold over the slots in LDS (the
+    // activation region, which no wave reads any more).
+    uint64_t* const kb = reinterpret_cast<uint64_t*>(lds_s);
+    const uint64_t k0 = __hip_atomic_load(keys + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t k1 = t + kThreads < (uint32_t)(kKeySlots - 1) * 16u
+                            ? __hip_atomic_load(keys + t + kThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : 0ull;
+    __hip_atomic_store(keys + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(keys + t + kThreads, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    kb[t] = k0 > k1 ? k0 : k1;
+    __syncthreads();
+    for (uint32_t half = kKeySlots / 4; half >= 1; half >>= 1) {
+      if (t < half * 16u) kb[t] = kb[t] > kb[t + half * 16u] ? kb[t] : kb[t + half * 16u];
+      __syncthreads();
+    }
+    if (t >= 64) return;  // no barrier follows
+    const int32_t gv = t < (uint32_t)M ? (int32_t)(0xFFFFFFFFu - (uint32_t)kb[t]) : 0;
+    if (t < (uint32_t)M) p.tree_greedy[t] = gv;
+    tree_walk_wave(M, par, dr, gv, p.tree_result);
   }
 }
 

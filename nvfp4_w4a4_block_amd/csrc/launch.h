@@ -58,9 +58,19 @@ struct GemmArgs {
   // every workgroup computes g_a = fl32(amax|A| / 2688) from the raw rows it
   // holds, uses it, and workgroup 0 stores it to *ga_dynamic.
   float* ga_dynamic = nullptr;
+  // Fused tree acceptance (persistent M = 16 stream only, with argmax_keys):
+  // when tree_result is set, the last workgroup to finish folds the keys,
+  // resets them to zero and runs the greedy acceptance of the M-node tree
+  // tree_parent / tree_draft, writing tree_greedy [M] and tree_result [3 + M]
+  // (the layout of tree_accept_kernel).  Word 0 of key slot kKeySlots - 1 is
+  // then its arrival counter (the kernel merges no key into that slot).
+  const int32_t* tree_parent = nullptr;
+  const int32_t* tree_draft = nullptr;
+  int32_t* tree_greedy = nullptr;
+  int32_t* tree_result = nullptr;
 };
 
-constexpr int kKeySlots = 64;  // argmax key slots per row
+constexpr int kKeySlots = 64;  // argmax key slots per row (zero between calls)
 
 // FP8 E4M3 KV-cache codec (kv_fp8.hip).
 hipError_t launch_kv_fp8_encode(const void* x, bool bf16, int64_t n, const float* scale, uint8_t* q,

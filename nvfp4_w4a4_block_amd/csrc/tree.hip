@@ -16,7 +16,9 @@
 // the 16 x vocabulary fp32 logits need not be written); argmax_rows_kernel
 // serves the shapes that kernel does not take, from logits already written.
 // The acceptance kernel folds the slots and resets them to zero, so the key
-// workspace needs clearing only before its first use.
+// workspace needs clearing only before its first use.  The persistent
+// weight-stream kernel (gemm_m16_stream.hip) runs the same fold, reset and
+// walk in its last workgroup instead.
 #include "device_common.h"
 #include "launch.h"
 
@@ -79,40 +81,7 @@ __global__ __launch_bounds__(1024) void tree_accept_kernel(int n, const int32_t*
   }
   if (t >= 64) return;  // no barrier follows
   if (greedy_out && t < n) greedy_out[t] = gv;
-  // The walk in node order, in scalar registers: node u reads its parent's
-  // acceptance bit, depth and greedy token across lanes.
-  uint64_t okm = 1;  // bit v: node v accepted (the root is)
-  int32_t depth_v = 0;  // lane v: depth of node v
-  int end = 0, dend = 0;
-  for (int u = 1; u < n; ++u) {
-    const int pu = __builtin_amdgcn_readlane(par, u);
-    const bool valid = pu >= 0 && pu < u;
-    const int ps = valid ? pu : 0;
-    const int d = valid ? __builtin_amdgcn_readlane(depth_v, ps) + 1 : 0;
-    depth_v = t == u ? d : depth_v;
-    const bool ok = valid && ((okm >> ps) & 1ull) &&
-                    __builtin_amdgcn_readlane(dr, u) == __builtin_amdgcn_readlane(gv, ps);
-    if (ok) {
-      okm |= 1ull << u;
-      if (d > dend) {
-        end = u;
-        dend = d;
-      }
-    }
-  }
-  // Lane i < L: the node at depth i + 1 on the root-to-end path; -1 beyond.
-  int32_t path_v = -1;
-  int u = end;
-  for (int i = dend - 1; i >= 0; --i) {
-    path_v = t == i ? u : path_v;
-    u = __builtin_amdgcn_readlane(par, u);
-  }
-  if (t == 0) {
-    result[0] = end;
-    result[1] = dend;
-    result[2] = __builtin_amdgcn_readlane(gv, end);
-  }
-  if (t < n) result[3 + t] = path_v;
+  tree_walk_wave(n, par, dr, gv, result);
 }
 
 }  // namespace

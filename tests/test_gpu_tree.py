@@ -182,3 +182,59 @@ def test_tree_verify_lm_head_full_size(want_logits):
         assert result.cpu().numpy().tolist() == [end, L, bonus] + path, (seed, draft)
         if want_logits:
             assert np.array_equal(np.argmax(logits.cpu().numpy(), axis=1), np.asarray(greedy_ref))
+
+
+def _stream_head(M, seed):
+    """Random NVFP4 operands of an M x 5120 x 70000 head: random activation codes and scale
+    bytes, random weight codes and moderate E4M3 scale bytes (2^-2 .. 2^1.875), drawn on the
+    device from a seeded generator."""
+    K, N = 5120, 70000
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    rnd = lambda lo, hi, shape: torch.randint(lo, hi, shape, dtype=torch.uint8, device="cuda", generator=gen)
+    ac, asc = rnd(0, 256, (M, K // 2)), rnd(0x28, 0x48, (M, K // 16))
+    wc, wsc = rnd(0, 256, (N, K // 2)), rnd(0x28, 0x48, (N, K // 16))
+    return ac, asc, U.scalar(np.float32(0.03)), wc, wsc, U.scalar(np.float32(0.0173))
+
+
+@pytest.mark.parametrize("M", [3, 9, 16])
+def test_tree_verify_fused_acceptance_on_weight_stream(M):
+    """At M x 5120 x 70000 the LM head runs on the persistent weight-stream kernel, whose last
+    workgroup to finish folds the argmax keys and runs the acceptance in the same launch.  On
+    random trees, the result equals the oracle's walk over the greedy tokens the call returns
+    (themselves the argmax of the logits the same kernel writes), every call returns the same
+    greedy tokens, and the key workspace (arrival counter included) is zero after every call."""
+    ops = _stream_head(M, 40 + M)
+    assert B.gemm_dispatch(M, 5120, 70000, 0) == B.KERNEL_M16_STREAM
+    N = 70000
+    keys = torch.zeros(1024, dtype=torch.int64, device="cuda")
+    g0, _, logits = B.nvfp4_tree_verify(*ops, i32([-1] + [0] * (M - 1)), i32([0] * M), want_logits=True, keys=keys)
+    g0 = g0.cpu().numpy()
+    assert np.array_equal(np.argmax(logits.cpu().numpy(), axis=1), g0)
+    assert int(keys.abs().sum()) == 0
+    rng = np.random.default_rng(M)
+    for trial in range(8):
+        parent = [-1] + [int(rng.integers(0, v)) for v in range(1, M)]
+        draft = [0] + [int(g0[parent[v]]) if rng.random() < 0.7 else int(g0[parent[v]] + 1) % N
+                       for v in range(1, M)]
+        greedy, result, _ = B.nvfp4_tree_verify(*ops, i32(parent), i32(draft), want_logits=bool(trial % 2),
+                                                keys=keys)
+        torch.cuda.synchronize()
+        assert greedy.cpu().numpy().tolist() == g0.tolist(), trial
+        end, L, bonus, path = expected_result(parent, draft, g0)
+        assert result.cpu().numpy().tolist() == [end, L, bonus] + path, (trial, parent, draft)
+        assert int(keys.abs().sum()) == 0, trial
+
+
+def test_tree_verify_fused_acceptance_rejects_invalid_parents():
+    """The weight-stream kernel's fused walk: parent indices outside [0, v) reject the node
+    even when its draft matches (the walk reads nothing outside the arrays)."""
+    ops = _stream_head(5, 77)
+    keys = torch.zeros(1024, dtype=torch.int64, device="cuda")
+    g, _, _ = B.nvfp4_tree_verify(*ops, i32([-1, 0, 1, 2, 3]), i32([0] * 5), keys=keys)
+    g = g.cpu().numpy().tolist()
+    parent = [-1, 0, 5, -7, 1]
+    draft = [0, g[0], g[0], g[0], g[1]]
+    greedy, result, _ = B.nvfp4_tree_verify(*ops, i32(parent), i32(draft), keys=keys)
+    assert greedy.cpu().numpy().tolist() == g
+    assert result.cpu().numpy().tolist() == [4, 2, g[4], 1, 4, -1, -1, -1]
+    assert int(keys.abs().sum()) == 0
