@@ -184,11 +184,10 @@ def test_tree_verify_lm_head_full_size(want_logits):
             assert np.array_equal(np.argmax(logits.cpu().numpy(), axis=1), np.asarray(greedy_ref))
 
 
-def _stream_head(M, seed):
-    """Random NVFP4 operands of an M x 5120 x 70000 head: random activation codes and scale
-    bytes, random weight codes and moderate E4M3 scale bytes (2^-2 .. 2^1.875), drawn on the
-    device from a seeded generator."""
-    K, N = 5120, 70000
+def _stream_head(M, seed, K=5120, N=70000):
+    """Random NVFP4 operands of an M x K x N head (default 5120 x 70000): random activation codes
+    and scale bytes, random weight codes and moderate E4M3 scale bytes (2^-2 .. 2^1.875), drawn
+    on the device from a seeded generator."""
     gen = torch.Generator(device="cuda").manual_seed(seed)
     rnd = lambda lo, hi, shape: torch.randint(lo, hi, shape, dtype=torch.uint8, device="cuda", generator=gen)
     ac, asc = rnd(0, 256, (M, K // 2)), rnd(0x28, 0x48, (M, K // 16))
@@ -238,3 +237,27 @@ def test_tree_verify_fused_acceptance_rejects_invalid_parents():
     assert greedy.cpu().numpy().tolist() == g
     assert result.cpu().numpy().tolist() == [4, 2, g[4], 1, 4, -1, -1, -1]
     assert int(keys.abs().sum()) == 0
+
+
+def test_tree_verify_fused_acceptance_with_more_workgroups_than_cus():
+    """16 x 1024 x 300000: 18750 groups of 16 rows, so the stream kernel's grid exceeds the CU
+    count and some workgroups start only after others have finished; the last to take its ticket
+    still sees every key.  Greedy tokens equal the argmax of the logits the same launch writes,
+    the result equals the oracle's walk over them, and the key workspace is zero afterwards."""
+    M, K, N = 16, 1024, 300000
+    assert B.gemm_dispatch(M, K, N, 0) == B.KERNEL_M16_STREAM
+    ops = _stream_head(M, 91, K, N)
+    keys = torch.zeros(1024, dtype=torch.int64, device="cuda")
+    g0, _, logits = B.nvfp4_tree_verify(*ops, i32([-1] + [0] * (M - 1)), i32([0] * M), want_logits=True, keys=keys)
+    g0 = g0.cpu().numpy()
+    assert np.array_equal(np.argmax(logits.cpu().numpy(), axis=1), g0)
+    del logits
+    parent = tree16()
+    draft = [0] + [int(g0[parent[v]]) if v % 3 else int(g0[parent[v]] + 1) % N for v in range(1, M)]
+    for rep in range(3):
+        greedy, result, _ = B.nvfp4_tree_verify(*ops, i32(parent), i32(draft), keys=keys)
+        torch.cuda.synchronize()
+        assert greedy.cpu().numpy().tolist() == g0.tolist(), rep
+        end, L, bonus, path = expected_result(parent, draft, g0)
+        assert result.cpu().numpy().tolist() == [end, L, bonus] + path, rep
+        assert int(keys.abs().sum()) == 0, rep
