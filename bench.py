@@ -11,7 +11,8 @@ MLPerf Edge Agentic Benchmark 6.4x Faster on Jetson AGX Thor" (section "Using NV
 accelerate Qwen3.6-27B inference"); the line's "workloads" object carries the M=16 records (the
 tree-verification down-projection, the LM head over the 16-node tree, the LM head with the fused
 greedy acceptance) and the M=512 suffix-prefill record (two GEMMs, the first emitting its output's
-NVFP4 form for the second).  --workload NAME measures one workload alone (one record as the line).
+NVFP4 form for the second).  --workload NAME measures one workload alone (one record as the line);
+--workload kv_fp8 measures the FP8 E4M3 KV-cache codec (its own metric, not part of the default line).
 
 A step is one pass of the workload's hot path over one batch of synthetic, seeded input already
 resident in HBM: activation quantization then the product(s).  Steps rotate over enough copies of
@@ -374,6 +375,72 @@ def bench_prefill(args, wl: WL.Workload) -> dict:
 # CPU oracle baseline
 # ---------------------------------------------------------------------------------------------
 
+KV_METRIC = "FP8 E4M3 KV-cache codec: HBM GB/s (bf16 in + E4M3 out, then back) & % peak"
+
+
+def bench_kv(args) -> dict:
+    """FP8 KV-cache codec (page section "Reusing KV cache across agent turns": the KV cache is kept
+    in FP8): a step encodes one layer's bf16 K and V (23,552 tokens x 8 heads x 128) to E4M3 with
+    a static calibrated scale and decodes them back to bf16, 6 bytes of HBM traffic per element
+    (2 + 1, then 1 + 2).  Input, code and output sets rotate so that the Infinity Cache cannot
+    serve them.  roofline: the encode kernel (3 bytes per element); roofline_decode: the decode."""
+    bits = WL.make_kv()
+    n = bits.size
+    x = torch.from_numpy(bits.view(np.int16).reshape(-1)).view(torch.bfloat16).to(DEV)
+    amax = float(torch.max(torch.abs(x.float())))
+    scale = torch.tensor([float(np.float32(np.float32(amax) / np.float32(448.0)))], device=DEV)  # calibration
+    R = max(2, math.ceil(ROTATE_BYTES / (6 * n)))
+    xs = [x] + [x.clone() for _ in range(R - 1)]
+    qs = [torch.empty(n, dtype=torch.uint8, device=DEV) for _ in range(R)]
+    ys = [torch.empty(n, dtype=torch.bfloat16, device=DEV) for _ in range(R)]
+    for i in range(R):  # codes to decode in the decode-only timing
+        B.nvfp4_kv_fp8_encode(xs[i], scale, qs[i])
+
+    def enc(i):
+        B.nvfp4_kv_fp8_encode(xs[i % R], scale, qs[i % R])
+
+    def dec(i):
+        B.nvfp4_kv_fp8_decode(qs[i % R], scale, torch.bfloat16, ys[i % R])
+
+    def step(i):
+        enc(i)
+        dec(i)
+
+    step_ms = timed(step, args.steps, args.warmup)
+    enc_ms = timed(enc, args.steps, args.warmup)
+    dec_ms = timed(dec, args.steps, args.warmup)
+    log(f"[bench] kv_fp8: n={n}, step {step_ms * 1e3:.2f} us, kv_encode_kernel {enc_ms * 1e3:.2f} us, "
+        f"kv_decode_kernel {dec_ms * 1e3:.2f} us per launch")
+    rec = {"metric": KV_METRIC, "value": 6.0 * n / (step_ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"kv_fp8: one layer's K and V, {WL.KV_TOKENS} tokens x {WL.KV_HEADS} heads x "
+                                  f"{WL.KV_DIM}, bf16 <-> E4M3", "elements": n, "copies": R,
+                      "step": "nvfp4_kv_fp8_encode + nvfp4_kv_fp8_decode", "parallelism": "none (1 GPU)"}}
+    rec["roofline"] = hbm_roofline("kv_encode_kernel (bf16 -> E4M3)", 3 * n, enc_ms, measured_traffic("kv_fp8"))
+    rec["roofline_decode"] = hbm_roofline("kv_decode_kernel (E4M3 -> bf16)", 3 * n, dec_ms, None)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = kv_cpu_baseline(bits, args.cpu_seconds)
+    return rec
+
+
+def kv_cpu_baseline(bits: np.ndarray, budget_s: float) -> dict:
+    """The oracle's encode + decode (NumPy) on the first 2^22 elements of the same layer."""
+    from oracle import kvfp8 as KVO
+    xs = WL.bf16_bits_to_f32(bits.reshape(-1)[: 1 << 22])
+    s = KVO.calibrated_scale(xs)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        KVO.decode_bf16_bits(KVO.encode(xs, s), s)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": 6.0 * xs.size * reps / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} x encode + decode of the first {xs.size} elements, {el:.1f} s (NumPy, one thread)",
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0))}
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -455,7 +522,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="all", choices=["all"] + sorted(WL.WORKLOADS))
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(WL.WORKLOADS) + ["kv_fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dynamic-act-scale", action="store_true",
                     help="decode: compute the activation scale on the device in every step (inside the fused "
@@ -486,6 +553,8 @@ def main() -> int:
             if name == "tree_verify":  # the LM-head weights are no longer needed
                 cache.clear()
             torch.cuda.empty_cache()
+    elif args.workload == "kv_fp8":
+        line = bench_kv(args)
     else:
         args.headline = args.workload
         line = run_workload(args, args.workload, cache)
