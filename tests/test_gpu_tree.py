@@ -195,16 +195,16 @@ def _stream_head(M, seed, K=5120, N=70000):
     return ac, asc, U.scalar(np.float32(0.03)), wc, wsc, U.scalar(np.float32(0.0173))
 
 
-@pytest.mark.parametrize("M", [3, 9, 16])
-def test_tree_verify_fused_acceptance_on_weight_stream(M):
-    """At M x 5120 x 70000 the LM head runs on the persistent weight-stream kernel, whose last
-    workgroup to finish folds the argmax keys and runs the acceptance in the same launch.  On
-    random trees, the result equals the oracle's walk over the greedy tokens the call returns
-    (themselves the argmax of the logits the same kernel writes), every call returns the same
-    greedy tokens, and the key workspace (arrival counter included) is zero after every call."""
-    ops = _stream_head(M, 40 + M)
-    assert B.gemm_dispatch(M, 5120, 70000, 0) == B.KERNEL_M16_STREAM
-    N = 70000
+@pytest.mark.parametrize("M,N", [(3, 70000), (9, 70000), (16, 70000), (11, 70003)])
+def test_tree_verify_fused_acceptance_on_weight_stream(M, N):
+    """At M x 5120 x N (N = 70000, or 70003 with a ragged last group of rows) the LM head runs on
+    the persistent weight-stream kernel, whose last workgroup to finish folds the argmax keys and
+    runs the acceptance in the same launch.  On random trees, the result equals the oracle's walk
+    over the greedy tokens the call returns (themselves the argmax of the logits the same kernel
+    writes), every call returns the same greedy tokens, and the key workspace (arrival counter
+    included) is zero after every call."""
+    ops = _stream_head(M, 40 + M, 5120, N)
+    assert B.gemm_dispatch(M, 5120, N, 0) == B.KERNEL_M16_STREAM
     keys = torch.zeros(1024, dtype=torch.int64, device="cuda")
     g0, _, logits = B.nvfp4_tree_verify(*ops, i32([-1] + [0] * (M - 1)), i32([0] * M), want_logits=True, keys=keys)
     g0 = g0.cpu().numpy()
