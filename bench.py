@@ -460,7 +460,7 @@ def cpu_baseline(wl: WL.Workload, budget_s: float) -> dict:
 
     from oracle import gemm as G
     from oracle import quant as Q
-    rows = 2048 if wl.M <= 16 else 256
+    rows = min(2048 if wl.M <= 16 else 256, wl.N)
     inp = WL.generate(wl)
     a = inp.a_f32()
     g_a = calibrated_scale(a)
